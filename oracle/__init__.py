@@ -1,0 +1,217 @@
+"""Decode-attention oracle: plain, slow, fp64 CPU definition of paged GQA/MQA decode
+attention, its split partials and their merge.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library in ``mqa_split_kv_amd`` and imports nothing from it; the two
+meet only through the seeded input generator ``mqa_split_kv_amd.synth`` (random
+draws, bf16 rounding and fp8 packing, no attention arithmetic).
+
+The arithmetic lives in ``oracle.c`` (compiled with gcc, loaded through ctypes);
+each function there cites the passage of the pages it follows.  ``plan.py`` holds
+the work-partition definitions the plan kernel must reproduce bit for bit.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+KV_BF16, KV_FP8_PAGE_HEAD, KV_MLA656 = 0, 1, 2
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("G", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("s_page", ctypes.c_int64), ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64),
+        ("kv_format", ctypes.c_int32),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+            "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        vp = ctypes.c_void_p
+        L.oracle_decode.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_double, vp, vp, vp, ctypes.c_int]
+        L.oracle_decode.restype = ctypes.c_int
+        L.oracle_ranges.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_double, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_int]
+        L.oracle_ranges.restype = ctypes.c_int
+        L.oracle_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+        L.oracle_merge.restype = None
+        L.oracle_e4m3_decode_n.argtypes = [vp, vp, ctypes.c_int64]
+        L.oracle_bf16_decode_n.argtypes = [vp, vp, ctypes.c_int64]
+        L.oracle_mla656_unpack_n.argtypes = [vp, vp, ctypes.c_int64]
+        L.oracle_threads.argtypes = [ctypes.c_int]
+        L.oracle_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if dtype is not None and a.dtype != dtype:
+        a = a.astype(dtype)
+    return np.ascontiguousarray(a)
+
+
+def _desc(case) -> _Desc:
+    return _Desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
+                 case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
+                 case["s_tok"], case["kv_format"])
+
+
+def _arrays(case):
+    q = _c(case["q"], np.uint16)
+    k = np.ascontiguousarray(case["k_pool"])
+    v = None if case.get("v_pool") is None else np.ascontiguousarray(case["v_pool"])
+    ks = _c(case.get("k_scale"), np.float32)
+    vs = _c(case.get("v_scale"), np.float32)
+    bt = _c(case["block_table"], np.int32)
+    return q, k, v, ks, vs, bt
+
+
+def threads(n: int = 0) -> int:
+    """Set (n > 0) and return the OpenMP thread count the oracle runs on."""
+    return lib().oracle_threads(n)
+
+
+def decode(case, scale=None, pairs=None, nthreads: int = 0):
+    """Plain definition for every (b, h) pair (or the boolean mask ``pairs`` [B, Hkv]).
+
+    Returns (out [B, Hq, Dv] float64, lse [B, Hq] float64); rows of skipped pairs are NaN.
+    """
+    B, Hkv, G, Dv = case["B"], case["Hkv"], case["G"], case["Dv"]
+    q, k, v, ks, vs, bt = _arrays(case)
+    sl = _c(case["seq_lens"], np.int32)
+    sc = float(case["scale"] if scale is None else scale)
+    mask = None if pairs is None else _c(np.asarray(pairs, dtype=bool).reshape(B, Hkv), np.uint8)
+    out = np.full((B, Hkv * G, Dv), np.nan)
+    lse = np.full((B, Hkv * G), np.nan)
+    d = _desc(case)
+    rc = lib().oracle_decode(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
+                             _ptr(bt), _ptr(sl), sc, _ptr(mask), _ptr(out), _ptr(lse), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle_decode failed")
+    return out, lse
+
+
+def ranges(case, rb, rt0, rt1, scale=None, nthreads: int = 0):
+    """Partial triples (m, l, Ot) of the XQA multi-block merge for token ranges.
+
+    rb, rt0, rt1: request index and [begin, end) token range of each range.
+    Returns m, l [n, Hkv, G] and Ot [n, Hkv, G, Dv] (unnormalised), float64.
+    """
+    Hkv, G, Dv = case["Hkv"], case["G"], case["Dv"]
+    q, k, v, ks, vs, bt = _arrays(case)
+    rb, rt0, rt1 = _c(rb, np.int32), _c(rt0, np.int32), _c(rt1, np.int32)
+    n = int(rb.shape[0])
+    m = np.zeros((n, Hkv, G))
+    l = np.zeros((n, Hkv, G))
+    Ot = np.zeros((n, Hkv, G, Dv))
+    sc = float(case["scale"] if scale is None else scale)
+    d = _desc(case)
+    rc = lib().oracle_ranges(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
+                             _ptr(bt), sc, n, _ptr(rb), _ptr(rt0), _ptr(rt1), _ptr(m), _ptr(l),
+                             _ptr(Ot), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle_ranges failed")
+    return m, l, Ot
+
+
+def merge(m, l, Ot):
+    """XQA merge of n partial triples.  m, l: [n, *rows]; Ot: [n, *rows, Dv].
+
+    Returns (O [*rows, Dv], lse [*rows]).
+    """
+    m = _c(m, np.float64)
+    l = _c(l, np.float64)
+    Ot = _c(Ot, np.float64)
+    n = m.shape[0]
+    rows_shape = m.shape[1:]
+    rows = int(np.prod(rows_shape)) if rows_shape else 1
+    Dv = Ot.shape[-1]
+    O = np.zeros(rows_shape + (Dv,))
+    lse = np.zeros(rows_shape)
+    lib().oracle_merge(n, rows, Dv, _ptr(m), _ptr(l), _ptr(Ot), _ptr(O), _ptr(lse))
+    return O, lse
+
+
+def split_decode(case, items, scale=None, nthreads: int = 0):
+    """Split-KV evaluation: partial triples per (request, token range) item, merged per
+    request with the XQA formula.  ``items`` is a list of (b, t0, t1).
+
+    Returns (out [B, Hq, Dv], lse [B, Hq]) and the per-item partials (m, l, Ot).
+    """
+    B, Hkv, G, Dv = case["B"], case["Hkv"], case["G"], case["Dv"]
+    rb = np.array([it[0] for it in items], np.int32)
+    rt0 = np.array([it[1] for it in items], np.int32)
+    rt1 = np.array([it[2] for it in items], np.int32)
+    m, l, Ot = ranges(case, rb, rt0, rt1, scale=scale, nthreads=nthreads)
+    out = np.zeros((B, Hkv * G, Dv))
+    lse = np.full((B, Hkv * G), -np.inf)
+    for b in range(B):
+        sel = np.nonzero(rb == b)[0]
+        if sel.size == 0:
+            continue
+        O, ls = merge(m[sel], l[sel], Ot[sel])
+        out[b] = O.reshape(Hkv * G, Dv)
+        lse[b] = ls.reshape(Hkv * G)
+    return out, lse, (m, l, Ot)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    o = np.zeros(c.shape)
+    lib().oracle_e4m3_decode_n(_ptr(c), _ptr(o), c.size)
+    return o
+
+
+def bf16_decode(bits) -> np.ndarray:
+    c = _c(bits, np.uint16)
+    o = np.zeros(c.shape)
+    lib().oracle_bf16_decode_n(_ptr(c), _ptr(o), c.size)
+    return o
+
+
+def mla656_unpack(tokens) -> np.ndarray:
+    """tokens: uint8 [..., 656] -> float64 [..., 576] (nope || rope)."""
+    t = _c(tokens, np.uint8)
+    n = t.size // 656
+    o = np.zeros(t.shape[:-1] + (576,))
+    lib().oracle_mla656_unpack_n(_ptr(t), _ptr(o), n)
+    return o

@@ -1,0 +1,365 @@
+/*
+ * Decode-attention oracle: the plain CPU definition of paged GQA/MQA decode
+ * attention, in fp64.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the product path never does.  It shares
+ * no code, header, table or constant with the HIP library.
+ *
+ * What it computes (source: "TensorRT-LLM 源码完全拆解(二十九): XQA 解码注意力内核",
+ * section 先把 decode 注意力的约束写清楚, the displayed equation):
+ *
+ *   out[b, h*G + g, :] = softmax( scale * q[b, h*G+g, :] . K_{b,h}^T ) V_{b,h}
+ *
+ * for every request b, KV head h and grouped query head g < G.  The query heads
+ * of one KV head are contiguous (same page, section "GQA 的组内复用", the output
+ * offset headGrpSize * idxHeadGrp + g).  K_{b,h} and V_{b,h} are the first
+ * seq_lens[b] tokens of the request, gathered page by page: token t lives in
+ * physical page block_table[b][t / P] at slot t % P (same page, section
+ * "分页 KV: 页号怎么变成 TMA 坐标").
+ *
+ * lse is the natural log of sum_t exp(scale * q . k_t) (the FlashMLA walk-through
+ * returns (o, lse) for merging; the pages do not define it further, so the plain
+ * log-sum-exp of the scaled logits is used).  An empty token range gives out = 0
+ * and lse = -inf.
+ *
+ * Pins: see tests/test_oracle.py (dense library attention, closed forms,
+ * invariances, the rescale worked example, all 256 e4m3 codes).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "oracle.h"
+
+/* ------------------------------------------------------------------------ */
+/* Element decoders                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 -> fp64: the 16 stored bits are the top half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary32 stored as 4 little-endian bytes -> fp64. */
+static double f32_bytes_to_f64(const uint8_t *p)
+{
+    float f;
+    memcpy(&f, p, sizeof f);
+    return (double)f;
+}
+
+/*
+ * OCP FP8 E4M3 ("e4m3fn", the float8_e4m3 of the pages) -> fp64.
+ * 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no infinities; the
+ * all-ones exponent+mantissa pattern (0x7F / 0xFF) is NaN; largest finite
+ * magnitude 448 (the XQA page's kE4M3_MAX, section "Hopper 路径上 V 不做显式反量化").
+ *   exponent field 0 : (-1)^s * 2^-6 * (m / 8)          (subnormal)
+ *   otherwise        : (-1)^s * 2^(e-7) * (1 + m / 8)
+ */
+double oracle_e4m3_to_f64(uint8_t code)
+{
+    int s = code >> 7;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/*
+ * MLA 656-byte token (FlashMLA walk-through, section 数据加载, byte-layout table):
+ *   bytes [0, 512)   : 512 e4m3 codes, the first 512 of the 576 latent dims
+ *   bytes [512, 528) : 4 fp32 scales, one per 128 consecutive codes
+ *   bytes [528, 656) : 64 bf16 values, the last 64 dims (rope part, not quantized)
+ * The key is the 576-vector nope || rope; the value is the first 512 dims
+ * (the value shares the dequantized latent with the key).
+ */
+void oracle_mla656_unpack(const uint8_t *tok, double *k576)
+{
+    for (int j = 0; j < 512; j++)
+        k576[j] = oracle_e4m3_to_f64(tok[j]) * f32_bytes_to_f64(tok + 512 + 4 * (j / 128));
+    for (int r = 0; r < 64; r++) {
+        uint16_t bits = (uint16_t)(tok[528 + 2 * r] | ((uint16_t)tok[528 + 2 * r + 1] << 8));
+        k576[512 + r] = oracle_bf16_to_f64(bits);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Token fetch through the block table                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Physical page and in-page slot of logical token t of request b. */
+static void locate(const oracle_desc *d, const int32_t *block_table, int b, int t,
+                   int64_t *page, int64_t *slot)
+{
+    *page = block_table[(int64_t)b * d->max_pages + t / d->page_size];
+    *slot = t % d->page_size;
+}
+
+/*
+ * Dequantised key (is_v = 0) or value (is_v = 1) vector of token t, KV head h,
+ * request b, written to x[0 .. D) or x[0 .. Dv).
+ *   bf16 : exact widening
+ *   fp8  : e4m3 code times the fp32 scale of that (page, KV head); K and V have
+ *          their own scale tables
+ *   MLA  : see oracle_mla656_unpack; V = first Dv dims of K
+ */
+static void fetch(const oracle_desc *d, const void *k_pool, const void *v_pool,
+                  const float *k_scale, const float *v_scale, const int32_t *block_table,
+                  int b, int h, int t, int is_v, double *x)
+{
+    int64_t page, slot;
+    locate(d, block_table, b, t, &page, &slot);
+    int64_t off = page * d->s_page + (int64_t)h * d->s_head + slot * d->s_tok;
+    int n = is_v ? d->Dv : d->D;
+    if (d->kv_format == ORACLE_KV_BF16) {
+        const uint16_t *p = (const uint16_t *)(is_v ? v_pool : k_pool) + off;
+        for (int i = 0; i < n; i++)
+            x[i] = oracle_bf16_to_f64(p[i]);
+    } else if (d->kv_format == ORACLE_KV_FP8_PAGE_HEAD) {
+        const uint8_t *p = (const uint8_t *)(is_v ? v_pool : k_pool) + off;
+        double s = (double)(is_v ? v_scale : k_scale)[page * d->Hkv + h];
+        for (int i = 0; i < n; i++)
+            x[i] = oracle_e4m3_to_f64(p[i]) * s;
+    } else {
+        double k576[576];
+        oracle_mla656_unpack((const uint8_t *)k_pool + off, k576);
+        for (int i = 0; i < n; i++)
+            x[i] = k576[i];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* One (range, KV head): the partial state of the XQA multi-block page       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For request b, KV head h and token range [t0, t1), compute for each grouped
+ * head g the partial triple of the XQA page (section "归约怎么记: 每个子序列一个
+ * 「和-最大值」对"):
+ *   m_g   = max_t s_t                          (local max)
+ *   l_g   = sum_t exp(s_t - m_g)               (local denominator)
+ *   Ot_g  = sum_t exp(s_t - m_g) * v_t         (local unnormalised output)
+ * with s_t = scale * q_g . k_t.  An empty range gives m = -inf, l = 0, Ot = 0.
+ * Two passes over the tokens: logits and their max first, then the weights.
+ */
+static int range_state(const oracle_desc *d, const uint16_t *q, const void *k_pool,
+                       const void *v_pool, const float *k_scale, const float *v_scale,
+                       const int32_t *block_table, double scale, int b, int h, int t0,
+                       int t1, double *m, double *l, double *Ot)
+{
+    const int G = d->G, D = d->D, Dv = d->Dv;
+    const int n = t1 > t0 ? t1 - t0 : 0;
+    for (int g = 0; g < G; g++) {
+        m[g] = -INFINITY;
+        l[g] = 0.0;
+        for (int i = 0; i < Dv; i++)
+            Ot[(int64_t)g * Dv + i] = 0.0;
+    }
+    if (n == 0)
+        return 0;
+
+    double *qf = (double *)malloc(sizeof(double) * (size_t)G * D);
+    double *s = (double *)malloc(sizeof(double) * (size_t)G * n);
+    double *x = (double *)malloc(sizeof(double) * (size_t)(D > Dv ? D : Dv));
+    if (!qf || !s || !x) {
+        free(qf);
+        free(s);
+        free(x);
+        return -1;
+    }
+    const int Hq = d->Hkv * G;
+    for (int g = 0; g < G; g++)
+        for (int i = 0; i < D; i++)
+            qf[(int64_t)g * D + i] = oracle_bf16_to_f64(q[((int64_t)b * Hq + (int64_t)h * G + g) * D + i]);
+
+    /* pass 1: logits */
+    for (int t = t0; t < t1; t++) {
+        fetch(d, k_pool, v_pool, k_scale, v_scale, block_table, b, h, t, 0, x);
+        for (int g = 0; g < G; g++) {
+            double acc = 0.0;
+            for (int i = 0; i < D; i++)
+                acc += qf[(int64_t)g * D + i] * x[i];
+            double st = scale * acc;
+            s[(int64_t)g * n + (t - t0)] = st;
+            if (st > m[g])
+                m[g] = st;
+        }
+    }
+    /* pass 2: weights, denominator, weighted values */
+    for (int t = t0; t < t1; t++) {
+        fetch(d, k_pool, v_pool, k_scale, v_scale, block_table, b, h, t, 1, x);
+        for (int g = 0; g < G; g++) {
+            double w = exp(s[(int64_t)g * n + (t - t0)] - m[g]);
+            l[g] += w;
+            for (int i = 0; i < Dv; i++)
+                Ot[(int64_t)g * Dv + i] += w * x[i];
+        }
+    }
+    free(qf);
+    free(s);
+    free(x);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public entry points                                                       */
+/* ------------------------------------------------------------------------ */
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+int oracle_threads(int nthreads) { return set_threads(nthreads); }
+
+/*
+ * Whole-request attention for every (b, h) with pair_mask[b*Hkv+h] != 0
+ * (pair_mask NULL: all pairs):  out = Ot / l,  lse = m + ln l.
+ * out is [B][Hq][Dv], lse is [B][Hq]; rows of skipped pairs are left untouched.
+ */
+int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
+                  const void *v_pool, const float *k_scale, const float *v_scale,
+                  const int32_t *block_table, const int32_t *seq_lens, double scale,
+                  const uint8_t *pair_mask, double *out, double *lse, int nthreads)
+{
+    const int B = d->B, Hkv = d->Hkv, G = d->G, Dv = d->Dv, Hq = Hkv * G;
+    int err = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t pr = 0; pr < (int64_t)B * Hkv; pr++) {
+        const int b = (int)(pr / Hkv), h = (int)(pr % Hkv);
+        if (pair_mask && !pair_mask[pr])
+            continue;
+        double *m = (double *)malloc(sizeof(double) * (size_t)G);
+        double *l = (double *)malloc(sizeof(double) * (size_t)G);
+        double *Ot = (double *)malloc(sizeof(double) * (size_t)G * Dv);
+        if (!m || !l || !Ot ||
+            range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h, 0,
+                        seq_lens[b], m, l, Ot) != 0) {
+            err |= 1;
+        } else {
+            for (int g = 0; g < G; g++) {
+                const int64_t row = (int64_t)b * Hq + (int64_t)h * G + g;
+                if (l[g] > 0.0) {
+                    for (int i = 0; i < Dv; i++)
+                        out[row * Dv + i] = Ot[(int64_t)g * Dv + i] / l[g];
+                    lse[row] = m[g] + log(l[g]);
+                } else {
+                    for (int i = 0; i < Dv; i++)
+                        out[row * Dv + i] = 0.0;
+                    lse[row] = -INFINITY;
+                }
+            }
+        }
+        free(m);
+        free(l);
+        free(Ot);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Partial triples for a list of n token ranges (request rb[i], tokens
+ * [rt0[i], rt1[i])), for every KV head:
+ *   m, l : [n][Hkv][G]     Ot : [n][Hkv][G][Dv]
+ */
+int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
+                  const void *v_pool, const float *k_scale, const float *v_scale,
+                  const int32_t *block_table, double scale, int n, const int32_t *rb,
+                  const int32_t *rt0, const int32_t *rt1, double *m, double *l, double *Ot,
+                  int nthreads)
+{
+    const int Hkv = d->Hkv, G = d->G, Dv = d->Dv;
+    int err = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t pr = 0; pr < (int64_t)n * Hkv; pr++) {
+        const int i = (int)(pr / Hkv), h = (int)(pr % Hkv);
+        if (range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, rb[i], h,
+                        rt0[i], rt1[i], m + pr * G, l + pr * G, Ot + pr * (int64_t)G * Dv) != 0)
+            err |= 1;
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Merge of n partial triples into one result, for `rows` independent rows of
+ * width Dv (XQA page, section "归约怎么记", the merge equation):
+ *   m   = max_i m_i
+ *   l   = sum_i l_i * exp(m_i - m)
+ *   O   = (1 / l) * sum_i Ot_i * exp(m_i - m)
+ * and lse = m + ln l.  Partials with m_i = -inf (empty ranges) carry no weight;
+ * if every partial is empty, O = 0 and lse = -inf (the rule of never forming
+ * -inf - (-inf), pipelining page, section 三, "分数可以早算").
+ *   m, l : [n][rows]   Ot : [n][rows][Dv]   O : [rows][Dv]   lse : [rows]
+ */
+void oracle_merge(int n, int rows, int Dv, const double *m, const double *l, const double *Ot,
+                  double *O, double *lse)
+{
+    for (int r = 0; r < rows; r++) {
+        double mm = -INFINITY;
+        for (int i = 0; i < n; i++)
+            if (m[(int64_t)i * rows + r] > mm)
+                mm = m[(int64_t)i * rows + r];
+        double *o = O + (int64_t)r * Dv;
+        for (int k = 0; k < Dv; k++)
+            o[k] = 0.0;
+        if (mm == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double ll = 0.0;
+        for (int i = 0; i < n; i++) {
+            double mi = m[(int64_t)i * rows + r];
+            if (mi == -INFINITY)
+                continue;
+            double w = exp(mi - mm);
+            ll += l[(int64_t)i * rows + r] * w;
+            const double *oti = Ot + ((int64_t)i * rows + r) * Dv;
+            for (int k = 0; k < Dv; k++)
+                o[k] += oti[k] * w;
+        }
+        for (int k = 0; k < Dv; k++)
+            o[k] /= ll;
+        lse[r] = mm + log(ll);
+    }
+}
+
+/* Vector helpers for the Python wrapper and the codec pins. */
+void oracle_e4m3_decode_n(const uint8_t *codes, double *outv, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        outv[i] = oracle_e4m3_to_f64(codes[i]);
+}
+
+void oracle_bf16_decode_n(const uint16_t *bits, double *outv, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        outv[i] = oracle_bf16_to_f64(bits[i]);
+}
+
+void oracle_mla656_unpack_n(const uint8_t *toks, double *k576, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        oracle_mla656_unpack(toks + i * 656, k576 + i * 576);
+}
