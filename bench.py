@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark: paged split-KV GQA decode attention on one MI355X.
+
+One step = pa_decode_run + pa_decode_combine (split-KV decode kernel + combine
+kernel) over the whole batch, on one stream, with every input resident in HBM; the
+plan is built once before timing (it is reusable while lengths are unchanged) and
+timed separately.  Default workload: GQA decode at a Llama-70B-like shape (B=32,
+Hq=64, Hkv=8, D=128, bf16 KV, 64-token pages, 4096 tokens each, balanced plan).
+
+Prints ONE JSON line.  `value` is the achieved algorithmic KV bandwidth (GB/s) of a
+whole step; `roofline` is for the dominant kernel (the decode kernel), timed with
+HIP events on the launch stream; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (default 1)")
+    ap.add_argument("--batch", type=int, default=None, help="batch of the HD64 workload (1 or 8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--graph", action="store_true", help="also time hipGraph replay of a step")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the split-KV path shards by request / KV head without any exchange, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mqa_split_kv_amd import binding as pb
+    from mqa_split_kv_amd import synth
+
+    torch.cuda.set_device(0)
+    t_gen = time.time()
+    case = synth.config_case(args.config, B=args.batch)
+    gen_s = time.time() - t_gen
+    print(f"[bench] generated workload {args.config} ({case['name']}) in {gen_s:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).cuda()
+
+    q, kp = dev(case["q"]), dev(case["k_pool"])
+    vp = dev(case["v_pool"]) if case.get("v_pool") is not None else None
+    ks = dev(case["k_scale"]) if case.get("k_scale") is not None else None
+    vs = dev(case["v_scale"]) if case.get("v_scale") is not None else None
+    bt, sl = dev(case["block_table"]), dev(case["seq_lens"])
+    B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
+    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    desc = pb.desc_from_case(case)
+    runner = pb.PagedDecode(desc)
+    stream = torch.cuda.current_stream()
+
+    # plan (once; timed separately)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runner.plan(sl)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        runner.plan(sl)
+    e1.record()
+    torch.cuda.synchronize()
+    plan_us = e0.elapsed_time(e1) * 1000.0 / 10
+
+    def step():
+        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs)
+        runner.combine(out, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps bracketed by synchronisation
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # dominant kernel alone: the decode kernel, back to back on the same stream
+    nk = max(args.steps, 50)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(nk):
+        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    decode_us = k0.elapsed_time(k1) * 1000.0 / nk
+    runner.combine(out, lse)
+    torch.cuda.synchronize()
+
+    graph_us = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1000.0 / args.steps
+
+    kv_bytes = synth.kv_bytes(case)
+    io = synth.io_bytes(case)
+    step_us = step_ms * 1000.0
+    gbs = kv_bytes / (step_us * 1e-6) / 1e9
+    dec_gbs = kv_bytes / (decode_us * 1e-6) / 1e9
+    fmt = {0: "bf16", 1: "fp8e4m3-kv/bf16", 2: "mla656-fp8/bf16"}[case["kv_format"]]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    cfg = {"workload": case["name"], "B": B, "Hq": Hq, "Hkv": case["Hkv"], "D": case["D"],
+           "Dv": Dv, "page_size": case["page_size"], "seq_len_total": int(np.sum(case["seq_lens"])),
+           "kv_format": fmt, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
+           "num_parts": pb.pa_decode_num_parts(desc), "parallelism": "single GPU"}
+    rec = {
+        "metric": "decode-attention µs/step + achieved KV HBM GB/s (% of MI355X peak)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "us_per_step": round(step_us, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case["kv_format"] == 0 else fmt,
+        "data": "synthetic (seeded N(0,1), random page permutation)",
+        "config": cfg,
+        "kv_bytes_per_step": kv_bytes,
+        "io_bytes_per_step": io,
+        "plan_us": round(plan_us, 2),
+        "decode_kernel_us": round(decode_us, 2),
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "wall_s_timed": round(wall_s, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(case, seconds):
+    """Time the fp64 CPU oracle on a bounded sample of (request, KV head) pairs."""
+    import numpy as np
+
+    import oracle
+    from mqa_split_kv_amd import synth
+
+    B, Hkv = case["B"], case["Hkv"]
+    threads = oracle.threads(0)
+    L = np.asarray(case["seq_lens"], np.int64)
+    order = [(b, h) for b in range(B) for h in range(Hkv)]
+    n = max(1, min(len(order), threads))
+    spent, done_pairs, done_tokens, reps = 0.0, 0, 0, 1
+    while True:
+        pairs = np.zeros((B, Hkv), bool)
+        sel = order[:n]
+        for b, h in sel:
+            pairs[b, h] = True
+        t0 = time.perf_counter()
+        oracle.decode(case, pairs=pairs)
+        dt = time.perf_counter() - t0
+        spent, done_pairs = dt, n
+        done_tokens = int(sum(L[b] for b, _ in sel))
+        if dt >= seconds or n == len(order):
+            break
+        n = min(len(order), max(n + 1, int(n * min(8.0, 1.5 * seconds / max(dt, 1e-3)))))
+    # the whole workload fits in the budget: repeat it until the budget is spent
+    while spent * reps < seconds and reps < 1000:
+        extra = max(1, int((seconds - spent * reps) / max(spent, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(extra):
+            oracle.decode(case, pairs=pairs)
+        dt = time.perf_counter() - t0
+        spent = (spent * reps + dt) / (reps + extra)
+        reps += extra
+    per_tok_head = synth.kv_bytes(case) / max(1, int(L.sum()) * Hkv)
+    gbs = done_tokens * per_tok_head / spent / 1e9
+    full_us = spent * 1e6 * (int(L.sum()) * Hkv) / max(1, done_tokens)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_pairs} of {B * Hkv} (request, KV head) pairs, {done_tokens} tokens, "
+                      f"{reps} run(s), {spent:.2f} s each; full step extrapolates to "
+                      f"{full_us / 1e6:.2f} s",
+            "us_per_step_extrapolated": round(full_us, 1)}
+
+
+if __name__ == "__main__":
+    main()

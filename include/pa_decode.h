@@ -1,0 +1,155 @@
+/*
+ * pa_decode.h - C ABI of libpa_decode.so: paged split-KV GQA/MQA decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TensorRT-LLM XQA article, "TensorRT-LLM 源码完全拆解(二十九):
+ * XQA 解码注意力内核", section 先把 decode 注意力的约束写清楚, its displayed
+ * equation): one new query token per request; for request b, KV head h and each
+ * of the G query heads g of that KV head,
+ *
+ *     out[b][h*G + g][:] = softmax(scale * q[b][h*G + g][:] . K_{b,h}^T) V_{b,h}
+ *
+ * where K_{b,h}, V_{b,h} are the first seq_lens[b] tokens of the request, stored
+ * in fixed-size pages of a pool and found through a per-request block table
+ * (same article, section "分页 KV: 页号怎么变成 TMA 坐标"; query heads of one KV
+ * head are contiguous, section "GQA 的组内复用").  lse[b][hq] is the natural-log
+ * log-sum-exp of the scaled logits (the FlashMLA walk-through returns (o, lse);
+ * section 调度).  A request of length 0 gets out = 0 and lse = -inf.
+ *
+ * The sequence is split into chunks processed in parallel, each leaving a partial
+ * (normalised output, lse) that a combine step merges (XQA article, section
+ * "多块模式: 把一条序列沿 KV 切成几段"; FlashAttention tiling page, section 5
+ * "Split-K 策略与 num_splits 启发式"; FlashMLA walk-through, sections 调度 and
+ * 合并与性能账本).  Three calls, all enqueued on the caller's stream:
+ *
+ *   pa_decode_plan     split scheduler: writes the plan (which token ranges of which
+ *                      request each workgroup processes) from device seq_lens
+ *   pa_decode_run      split-KV decode kernel: writes final rows for requests done
+ *                      in one chunk, partials (workspace) for the others
+ *   pa_decode_combine  LSE-weighted merge of the partials into out / lse
+ *
+ * Ownership: the caller allocates and owns every buffer (device memory for all
+ * array arguments).  The library never allocates, frees or synchronises; it keeps
+ * no state except a per-device compute-unit count.  Calls on one stream are
+ * ordered by that stream; concurrent calls on different streams must not share a
+ * plan, workspace or output buffer.
+ *
+ * Errors: arguments are validated on the host before anything is launched; a
+ * non-PA_OK status means nothing was enqueued.  Device-side data (page ids,
+ * seq_lens) is trusted, not checked: every page id a request can reach must be
+ * < num_pages and seq_lens[b] <= max_pages_per_seq * page_size.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID = 1,      /* null pointer, non-positive size, misaligned pointer/stride */
+    PA_ERR_UNSUPPORTED = 2,  /* a valid shape this build has no kernel for */
+    PA_ERR_SIZE = 3,         /* plan or workspace smaller than the size query returned */
+    PA_ERR_DEVICE = 4        /* a HIP call (device query, kernel launch) failed */
+} pa_status;
+
+typedef enum {
+    /* bf16 K and V pools */
+    PA_KV_BF16 = 0,
+    /* OCP float8 e4m3 K and V pools; value = code * scale[page][kv_head], with separate
+       fp32 scale tables for K and V (k_scale, v_scale: [num_pages][Hkv]) */
+    PA_KV_FP8_E4M3_PAGE_HEAD = 1,
+    /* MLA latent cache, 656 bytes per token (FlashMLA walk-through, section 数据加载):
+       512 e4m3 codes | 4 fp32 scales (one per 128 codes) | 64 bf16 rope values.
+       K = the 576 dequantised values, V = their first 512; v_pool must be NULL. */
+    PA_KV_MLA656 = 2
+} pa_kv_format;
+
+typedef struct {
+    int32_t B;                 /* requests (one query token each) */
+    int32_t Hkv;               /* KV heads; query heads Hq = Hkv * G */
+    int32_t G;                 /* query heads per KV head (GQA group size; Hkv = 1: MQA) */
+    int32_t D;                 /* q / K head dim: 64 or 128 (bf16, fp8), 576 (MLA) */
+    int32_t Dv;                /* V / out head dim: = D, or 512 for MLA */
+    int32_t page_size;         /* tokens per page: 16, 32, 64, 128 or 256 */
+    int32_t num_pages;         /* pages in the pool */
+    int32_t max_pages_per_seq; /* columns of block_table */
+    /* pool strides in storage units (bf16: 2-byte elements; fp8 and MLA: bytes).
+       Token t of request b, KV head h starts at
+       pool + page * s_page + h * s_head + (t % page_size) * s_tok
+       with page = block_table[b][t / page_size].  HND [page][Hkv][P][D]:
+       s_page = Hkv*P*D, s_head = P*D, s_tok = D.  NHD [page][P][Hkv][D]:
+       s_page = P*Hkv*D, s_head = D, s_tok = Hkv*D.  MLA: s_tok = 656, s_head unused.
+       Every stride times the unit size must be a multiple of 16 bytes. */
+    int64_t s_page, s_head, s_tok;
+    int32_t q_len;             /* query tokens per request: must be 1 */
+    int32_t num_splits;        /* 0: balanced split scheduling; s > 0: s chunks per request */
+    int32_t kv_format;         /* pa_kv_format */
+    int32_t reserved;          /* must be 0 */
+} pa_decode_desc;
+
+/*
+ * Split scheduler.  With plan == NULL: size query only - writes the plan and
+ * workspace sizes in bytes (either pointer may be NULL), touches no device memory.
+ * Otherwise enqueues the plan kernel on `stream` (a hipStream_t; NULL = default
+ * stream), which reads seq_lens[B] (int32, device) and writes the plan.
+ * *plan_bytes must then hold the plan buffer's size (PA_ERR_SIZE if smaller).
+ *
+ * num_splits = s > 0: request b is cut into s chunks of ceil(ceil(L_b/64)/s)
+ * 64-token tiles each (FlashAttention tiling page, section 5.3; trailing chunks may
+ * be empty).  num_splits = 0: the tiles of all requests are laid end to end and cut
+ * into equal contiguous parts, one workgroup per (part, KV head), a few per compute
+ * unit (FlashMLA walk-through, section 调度); a request is cut where a part ends.
+ *
+ * The plan stays valid while the desc and seq_lens are unchanged, so one plan can
+ * serve every layer of a decode step.
+ */
+pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, void *plan,
+                         size_t *plan_bytes, size_t *workspace_bytes, void *stream);
+
+/*
+ * Split-KV decode.  Enqueues the decode kernel.
+ *   q           [B][Hq][D] bf16
+ *   k_pool      K pool (or the MLA656 pool), layout given by the desc strides
+ *   v_pool      V pool; NULL for PA_KV_MLA656
+ *   k_scale, v_scale  [num_pages][Hkv] fp32 for PA_KV_FP8_E4M3_PAGE_HEAD, else NULL
+ *   block_table [B][max_pages_per_seq] int32; seq_lens [B] int32 (must be the values
+ *               the plan was built from)
+ *   scale       logit scale; <= 0 selects 1/sqrt(D)
+ *   out         [B][Hq][Dv] bf16; lse [B][Hq] fp32 (natural log)
+ *   plan        written by pa_decode_plan for the same desc
+ *   workspace   >= the size pa_decode_plan reported (fp32 partials), 16-byte aligned
+ * Rows of requests that the plan cuts into several chunks are only complete after
+ * pa_decode_combine.
+ */
+pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void *q,
+                        const void *k_pool, const void *v_pool, const float *k_scale,
+                        const float *v_scale, const int32_t *block_table,
+                        const int32_t *seq_lens, float scale, void *out, float *lse,
+                        void *workspace, void *stream);
+
+/*
+ * Combine.  For every request cut into several chunks (and every request of length
+ * 0) merges the chunk partials: M = max_i lse_i, lse = M + ln sum_i exp(lse_i - M),
+ * out = sum_i exp(lse_i - lse) * O_i (XQA article, section "归约怎么记", merge
+ * equation, written for normalised partials).  Requests done in one chunk are left
+ * as pa_decode_run wrote them.  A no-op launch-free call when num_splits == 1.
+ */
+pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
+                            void *out, float *lse, void *stream);
+
+/* Number of workgroups along the part axis that pa_decode_run launches for `desc`
+   on the current device (B * num_splits, or the balanced part count). */
+pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts);
+
+/* Static string for a status code. */
+const char *pa_status_string(pa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_DECODE_H */

@@ -1,15 +1,8 @@
 """MI355X-native paged split-KV GQA/MQA decode attention.
 
-The compute path is the C-ABI library ``libpa_decode.so`` (hand-written HIP for
-gfx950, built from ``csrc/``); ``binding`` wraps its three entry points with the
-same names for PyTorch device tensors.  ``synth`` draws seeded synthetic inputs.
-The binding is imported on first use so that ``synth`` can be used without a GPU.
+The compute path is the C-ABI library ``lib/libpa_decode.so`` (hand-written HIP for
+gfx950, built from ``csrc/`` by ``build.py``); ``binding`` wraps its entry points
+with the same names for PyTorch device tensors.  ``synth`` draws seeded synthetic
+inputs.  Submodules are imported explicitly (``from mqa_split_kv_amd import
+binding``), so ``synth`` can be used on a machine without a GPU.
 """
-__all__ = ["binding", "synth"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding as _b
-        return _b
-    raise AttributeError(name)

@@ -1,0 +1,227 @@
+// Host side of libpa_decode.so: argument validation, size queries and kernel launches
+// for the three C entry points declared in include/pa_decode.h.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::PlanLayout;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (queried once per device).
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < kMaxDevices) {
+        int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+        return -1;
+    if (dev < kMaxDevices) g_cu_count[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int elem_bytes(int fmt) { return fmt == PA_KV_BF16 ? 2 : 1; }
+
+// Shape checks shared by all entry points (no pointers).
+pa_status check_desc(const pa_decode_desc *d)
+{
+    if (!d) return PA_ERR_INVALID;
+    if (d->B <= 0 || d->Hkv <= 0 || d->G <= 0 || d->D <= 0 || d->Dv <= 0) return PA_ERR_INVALID;
+    if (d->page_size <= 0 || d->num_pages <= 0 || d->max_pages_per_seq <= 0) return PA_ERR_INVALID;
+    if (d->s_page < 0 || d->s_head < 0 || d->s_tok <= 0) return PA_ERR_INVALID;
+    if (d->num_splits < 0 || d->reserved != 0 || d->q_len <= 0) return PA_ERR_INVALID;
+    if (d->kv_format != PA_KV_BF16 && d->kv_format != PA_KV_FP8_E4M3_PAGE_HEAD &&
+        d->kv_format != PA_KV_MLA656)
+        return PA_ERR_INVALID;
+    const int64_t eb = elem_bytes(d->kv_format);
+    if ((d->s_page * eb) % 16 || (d->s_head * eb) % 16 || (d->s_tok * eb) % 16) return PA_ERR_INVALID;
+    if ((int64_t)d->Hkv * d->G > 65536) return PA_ERR_UNSUPPORTED;
+    if (d->q_len != 1) return PA_ERR_UNSUPPORTED;
+    const int P = d->page_size;
+    if (P != 16 && P != 32 && P != 64 && P != 128 && P != 256) return PA_ERR_UNSUPPORTED;
+    if (d->B > pa::kMaxBatch) return PA_ERR_UNSUPPORTED;
+    if (d->num_splits > 256) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)d->max_pages_per_seq * P > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
+    if (d->kv_format == PA_KV_MLA656) {
+        if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
+        return PA_ERR_UNSUPPORTED;   // no kernel for this format in this build yet
+    }
+    if (d->D != d->Dv || (d->D != 64 && d->D != 128)) return PA_ERR_UNSUPPORTED;
+    if (d->G > 16) return PA_ERR_UNSUPPORTED;
+    // a token row must fit inside the stride it is read with
+    if (d->s_tok < d->D) return PA_ERR_INVALID;
+    return PA_OK;
+}
+
+// Workgroups along the part axis.  Balanced rule: a few workgroups per compute unit
+// over all KV heads, so that every unit gets an equal share of each head's tiles.
+pa_status num_parts_for(const pa_decode_desc *d, int *np)
+{
+    if (d->num_splits > 0) {
+        *np = d->B * d->num_splits;
+        return PA_OK;
+    }
+    const int cu = cu_count();
+    if (cu <= 0) return PA_ERR_DEVICE;
+    const int wgs_per_cu = 2;
+    int n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
+    *np = n < 1 ? 1 : n;
+    return PA_OK;
+}
+
+pa_status layout_for(const pa_decode_desc *d, PlanLayout *L)
+{
+    int np = 0;
+    pa_status st = num_parts_for(d, &np);
+    if (st != PA_OK) return st;
+    *L = pa::plan_layout(d->B, d->num_splits, np);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(pa_status s)
+{
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case PA_ERR_SIZE: return "plan or workspace buffer too small";
+    case PA_ERR_DEVICE: return "HIP device error";
+    }
+    return "unknown status";
+}
+
+pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (!num_parts) return PA_ERR_INVALID;
+    int np = 0;
+    st = num_parts_for(desc, &np);
+    if (st == PA_OK) *num_parts = np;
+    return st;
+}
+
+pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, void *plan,
+                         size_t *plan_bytes, size_t *workspace_bytes, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    PlanLayout L;
+    st = layout_for(desc, &L);
+    if (st != PA_OK) return st;
+    const size_t pbytes = L.words * 4;
+    const size_t wbytes = pa::ws_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv);
+    if (!plan) {
+        if (plan_bytes) *plan_bytes = pbytes;
+        if (workspace_bytes) *workspace_bytes = wbytes;
+        return PA_OK;
+    }
+    if (!seq_lens || !plan_bytes) return PA_ERR_INVALID;
+    if (((uintptr_t)plan & 3) || ((uintptr_t)seq_lens & 3)) return PA_ERR_INVALID;
+    if (*plan_bytes < pbytes) return PA_ERR_SIZE;
+    if (workspace_bytes) *workspace_bytes = wbytes;
+    if (pa::launch_plan(seq_lens, (int32_t *)plan, L, desc->num_splits, (hipStream_t)stream) !=
+        hipSuccess)
+        return PA_ERR_DEVICE;
+    return PA_OK;
+}
+
+pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void *q,
+                        const void *k_pool, const void *v_pool, const float *k_scale,
+                        const float *v_scale, const int32_t *block_table,
+                        const int32_t *seq_lens, float scale, void *out, float *lse,
+                        void *workspace, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (!plan || !q || !k_pool || !block_table || !seq_lens || !out || !lse)
+        return PA_ERR_INVALID;
+    const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
+    if (!v_pool) return PA_ERR_INVALID;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+        ((uintptr_t)lse & 3) || ((uintptr_t)plan & 3) || ((uintptr_t)block_table & 3))
+        return PA_ERR_INVALID;
+    PlanLayout L;
+    st = layout_for(desc, &L);
+    if (st != PA_OK) return st;
+    const bool needs_ws = !(desc->num_splits == 1);
+    if (needs_ws && (!workspace || !aligned16(workspace))) return PA_ERR_INVALID;
+    if (!isfinite(scale)) return PA_ERR_INVALID;
+
+    pa::DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    const int64_t eb = elem_bytes(desc->kv_format);
+    a.q = (const uint16_t *)q;
+    a.k_pool = (const uint8_t *)k_pool;
+    a.v_pool = (const uint8_t *)v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.plan = (const int32_t *)plan;
+    a.out = (uint16_t *)out;
+    a.lse = lse;
+    a.ws_o = (float *)workspace;
+    a.ws_lse = workspace ? (float *)((uint8_t *)workspace +
+                                     pa::ws_o_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv))
+                         : nullptr;
+    a.s_page_b = desc->s_page * eb;
+    a.s_head_b = desc->s_head * eb;
+    a.s_tok_b = desc->s_tok * eb;
+    a.B = desc->B;
+    a.Hkv = desc->Hkv;
+    a.G = desc->G;
+    a.D = desc->D;
+    a.Dv = desc->Dv;
+    a.max_pages = desc->max_pages_per_seq;
+    a.page_shift = __builtin_ctz((unsigned)desc->page_size);
+    a.num_parts = L.num_parts;
+    a.part_begin_off = L.part_begin_off;
+    a.items_off = L.items_off;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)desc->D);
+    a.scale_log2 = sc * 1.4426950408889634f;
+    a.kv_format = desc->kv_format;
+    if (pa::launch_decode(a, (hipStream_t)stream) != hipSuccess) return PA_ERR_DEVICE;
+    return PA_OK;
+}
+
+pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
+                            void *out, float *lse, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (!plan || !out || !lse) return PA_ERR_INVALID;
+    if (desc->num_splits == 1) return PA_OK;     // every request is a single chunk
+    if (!workspace || !aligned16(workspace) || !aligned16(out) || ((uintptr_t)lse & 3))
+        return PA_ERR_INVALID;
+    PlanLayout L;
+    st = layout_for(desc, &L);
+    if (st != PA_OK) return st;
+    const float *ws_o = (const float *)workspace;
+    const float *ws_lse = (const float *)((const uint8_t *)workspace +
+                                          pa::ws_o_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv));
+    if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, (uint16_t *)out, lse, desc->B,
+                           desc->Hkv, desc->G, desc->Dv, L.chunk_off_off,
+                           (hipStream_t)stream) != hipSuccess)
+        return PA_ERR_DEVICE;
+    return PA_OK;
+}
+
+}  // extern "C"

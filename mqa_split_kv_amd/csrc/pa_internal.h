@@ -1,0 +1,88 @@
+// Internal declarations shared by the host API and the kernel translation units of
+// libpa_decode.so.  Each kernel file defines its kernels and the host launcher that
+// starts them; nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pa_decode.h"
+
+namespace pa {
+
+// Scheduling granule: a request's tokens are cut into chunks at multiples of this.
+constexpr int kTileTokens = 64;
+constexpr int kPlanMagic = 0x50414450;
+constexpr int kPlanHeaderWords = 8;
+constexpr int kMaxBatch = 4096;       // plan kernel keeps per-request prefix sums in LDS
+
+// Plan buffer (int32 words):
+//   [0] magic  [1] mode (0 fixed splits, 1 balanced)  [2] B  [3] num_parts
+//   [4] num_items  [5] tile tokens  [6] max_items  [7] 0
+//   part_begin[num_parts + 1] | chunk_off[B + 1] | items[max_items][4] = {b, tok0, tok1, flags}
+//   flags bit 0: the item is its request's only chunk and writes the final row.
+struct PlanLayout {
+    int mode;
+    int B;
+    int num_parts;
+    int max_items;
+    int part_begin_off;
+    int chunk_off_off;
+    int items_off;
+    size_t words;
+};
+
+inline PlanLayout plan_layout(int B, int num_splits, int num_parts)
+{
+    PlanLayout L;
+    L.mode = num_splits > 0 ? 0 : 1;
+    L.B = B;
+    L.num_parts = num_parts;
+    L.max_items = num_splits > 0 ? B * num_splits : num_parts + B;
+    L.part_begin_off = kPlanHeaderWords;
+    L.chunk_off_off = L.part_begin_off + num_parts + 1;
+    L.items_off = L.chunk_off_off + B + 1;
+    L.words = (size_t)L.items_off + 4 * (size_t)L.max_items;
+    return L;
+}
+
+// Workspace: normalised fp32 partial outputs [max_items][Hkv][G][Dv], then (256-byte
+// aligned) fp32 partial lse [max_items][Hkv][G] in natural log.
+inline size_t ws_o_bytes(int max_items, int Hkv, int G, int Dv)
+{
+    size_t b = (size_t)max_items * Hkv * G * Dv * 4;
+    return (b + 255) & ~(size_t)255;
+}
+inline size_t ws_bytes(int max_items, int Hkv, int G, int Dv)
+{
+    return ws_o_bytes(max_items, Hkv, G, Dv) + (size_t)max_items * Hkv * G * 4;
+}
+
+struct DecodeArgs {
+    const uint16_t *q;          // [B][Hq][D] bf16
+    const uint8_t *k_pool;      // byte pointers; strides below are in bytes
+    const uint8_t *v_pool;
+    const float *k_scale;       // [num_pages][Hkv] (fp8 formats)
+    const float *v_scale;
+    const int32_t *block_table; // [B][max_pages]
+    const int32_t *plan;
+    uint16_t *out;              // [B][Hq][Dv] bf16
+    float *lse;                 // [B][Hq]
+    float *ws_o;
+    float *ws_lse;
+    int64_t s_page_b, s_head_b, s_tok_b;   // pool strides in bytes
+    int B, Hkv, G, D, Dv, max_pages, page_shift;
+    int num_parts, part_begin_off, items_off;
+    float scale_log2;           // logit scale * log2(e)
+    int kv_format;
+};
+
+hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout &L,
+                       int num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
+                          uint16_t *out, float *lse, int B, int Hkv, int G, int Dv,
+                          int chunk_off_off, hipStream_t stream);
+
+}  // namespace pa

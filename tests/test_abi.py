@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point its
+header declares, and rejects bad arguments with the documented status before any
+HIP call (so these run on a machine without a GPU)."""
+import ctypes
+import re
+
+import pytest
+
+from mqa_split_kv_amd import binding as pb
+
+
+def _declared():
+    src = open(pb.HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status|const char \*)\s*(pa_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert set(_declared()) == set(pb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pb.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in range(5):
+        assert pb.status_string(s)
+    assert pb.status_string(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(B=2, Hkv=1, G=8, D=64, Dv=64, page_size=16, num_pages=40, max_pages_per_seq=17,
+                s_page=16 * 64, s_head=16 * 64, s_tok=64, num_splits=1, kv_format=pb.PA_KV_BF16)
+    base.update(kw)
+    return pb.make_desc(**base)
+
+
+def _plan_status(desc):
+    pbytes = ctypes.c_size_t(0)
+    wbytes = ctypes.c_size_t(0)
+    return pb.lib().pa_decode_plan(ctypes.byref(desc), None, None, ctypes.byref(pbytes),
+                                   ctypes.byref(wbytes), None), pbytes.value, wbytes.value
+
+
+BAD = [
+    (dict(B=0), pb.PA_ERR_INVALID),
+    (dict(G=0), pb.PA_ERR_INVALID),
+    (dict(Hkv=-1), pb.PA_ERR_INVALID),
+    (dict(page_size=0), pb.PA_ERR_INVALID),
+    (dict(s_tok=4), pb.PA_ERR_INVALID),          # 8-byte stride: not 16-byte aligned
+    (dict(s_tok=56), pb.PA_ERR_INVALID),         # not a multiple of 16 bytes... 112 B
+    (dict(num_splits=-1), pb.PA_ERR_INVALID),
+    (dict(kv_format=7), pb.PA_ERR_INVALID),
+    (dict(D=96, Dv=96, s_tok=96, s_head=16 * 96, s_page=16 * 96), pb.PA_ERR_UNSUPPORTED),
+    (dict(D=128, Dv=64), pb.PA_ERR_UNSUPPORTED),
+    (dict(page_size=8), pb.PA_ERR_UNSUPPORTED),
+    (dict(page_size=48), pb.PA_ERR_UNSUPPORTED),
+    (dict(G=17), pb.PA_ERR_UNSUPPORTED),
+    (dict(q_len=2), pb.PA_ERR_UNSUPPORTED),
+    (dict(B=5000), pb.PA_ERR_UNSUPPORTED),
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
+     pb.PA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_invalid_descriptors_rejected_on_host(kw, status):
+    st, _, _ = _plan_status(_desc(**kw))
+    assert st == status
+
+
+def test_size_query_fixed_splits_needs_no_device():
+    # fixed split counts do not depend on the device, so the size query is pure host logic
+    st, pbytes, wbytes = _plan_status(_desc(num_splits=2))
+    assert st == pb.PA_OK
+    B, s = 2, 2
+    assert pbytes == 4 * (8 + (B * s + 1) + (B + 1) + 4 * B * s)
+    o = (B * s * 1 * 8 * 64 * 4 + 255) // 256 * 256
+    assert wbytes == o + B * s * 1 * 8 * 4
+
+
+def test_run_rejects_null_and_misaligned_pointers():
+    L = pb.lib()
+    d = _desc()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    p = ctypes.c_void_p
+    args_ok = [p(base)] * 9
+    # null plan
+    st = L.pa_decode_run(ctypes.byref(d), None, *[p(base)] * 7, ctypes.c_float(0.0), p(base),
+                         p(base), p(base), None)
+    assert st == pb.PA_ERR_INVALID
+    # misaligned q
+    st = L.pa_decode_run(ctypes.byref(d), p(base), p(base + 2), *[p(base)] * 6,
+                         ctypes.c_float(0.0), p(base), p(base), p(base), None)
+    assert st == pb.PA_ERR_INVALID
+    # non-finite scale
+    st = L.pa_decode_run(ctypes.byref(d), *args_ok[:8], ctypes.c_float(float("nan")), p(base),
+                         p(base), p(base), None)
+    assert st == pb.PA_ERR_INVALID
+    # fp8 without scale tables
+    d8 = _desc(kv_format=pb.PA_KV_FP8_E4M3_PAGE_HEAD, s_tok=64, s_head=16 * 64, s_page=16 * 64)
+    st = L.pa_decode_run(ctypes.byref(d8), *[p(base)] * 4, None, None, p(base), p(base),
+                         ctypes.c_float(0.0), p(base), p(base), p(base), None)
+    assert st == pb.PA_ERR_INVALID
+
+
+def test_plan_size_check():
+    L = pb.lib()
+    d = _desc(num_splits=2)
+    buf = ctypes.create_string_buffer(4096)
+    small = ctypes.c_size_t(8)
+    wb = ctypes.c_size_t(0)
+    st = L.pa_decode_plan(ctypes.byref(d), ctypes.c_void_p(ctypes.addressof(buf)),
+                          ctypes.c_void_p(ctypes.addressof(buf)), ctypes.byref(small),
+                          ctypes.byref(wb), None)
+    assert st == pb.PA_ERR_SIZE
