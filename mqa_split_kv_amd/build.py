@@ -22,6 +22,8 @@ LIB = os.path.join(LIBDIR, "libpa_decode.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["pa_api.cpp", "pa_plan.hip", "pa_decode_kernel.hip", "pa_combine.hip"]
+PROBE_SOURCES = ["pa_probe.hip"]
+PROBE_LIB = os.path.join(LIBDIR, "libpa_probe.so")
 ARCH = "gfx950"
 
 
@@ -49,19 +51,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libpa_decode.so (the decode path) and libpa_probe.so (measurement helpers)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(5, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

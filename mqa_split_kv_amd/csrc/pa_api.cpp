@@ -66,8 +66,10 @@ pa_status check_desc(const pa_decode_desc *d)
     return PA_OK;
 }
 
-// Workgroups along the part axis.  Balanced rule: a few workgroups per compute unit
-// over all KV heads, so that every unit gets an equal share of each head's tiles.
+// Workgroups along the part axis.  Balanced rule: one workgroup per compute unit over
+// all KV heads, so that every unit gets an equal share of each head's tiles.  One
+// 4-wave workgroup per unit already keeps enough KV loads in flight to stream at the
+// HBM read ceiling; more parts would only cut requests into more chunks to merge.
 pa_status num_parts_for(const pa_decode_desc *d, int *np)
 {
     if (d->num_splits > 0) {
@@ -76,7 +78,7 @@ pa_status num_parts_for(const pa_decode_desc *d, int *np)
     }
     const int cu = cu_count();
     if (cu <= 0) return PA_ERR_DEVICE;
-    const int wgs_per_cu = 2;
+    const int wgs_per_cu = 1;
     int n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
     *np = n < 1 ? 1 : n;
     return PA_OK;

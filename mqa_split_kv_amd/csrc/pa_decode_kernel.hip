@@ -41,11 +41,27 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
+// Cache policy bits of the KV buffer loads.  2 = non-temporal: every KV byte is read
+// exactly once, so streaming it past the caches keeps them for the tables and partials
+// (the analogue of the evict-first hint in the FlashMLA walk-through, section 数据加载);
+// measured +11% bandwidth over the default policy on the Llama-70B-like workload.
+#ifndef PA_KV_LOAD_AUX
+#define PA_KV_LOAD_AUX 2
+#endif
+// Register ring depth (blocks) and the token-row byte threshold at or above which a
+// wave iteration covers 16 tokens instead of 32.
+#ifndef PA_RING_DEPTH
+#define PA_RING_DEPTH 4
+#endif
+#ifndef PA_BT16_MIN_ROW_BYTES
+#define PA_BT16_MIN_ROW_BYTES 256
+#endif
+
 template <int D, bool FP8>
 struct Cfg {
     static constexpr int EB = FP8 ? 1 : 2;            // stored bytes per element
     static constexpr int ROWB = D * EB;               // bytes of one token row
-    static constexpr int BT = ROWB >= 256 ? 16 : 32;  // tokens per wave iteration
+    static constexpr int BT = ROWB >= PA_BT16_MIN_ROW_BYTES ? 16 : 32;  // tokens per wave iteration
     static constexpr int NSB = BT / 16;               // 16-token MFMA row blocks per iteration
     static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
     static constexpr int NLD = CPR / 4;               // K (and V) loads per lane per sub-block
@@ -53,7 +69,7 @@ struct Cfg {
     static constexpr int NDB = D / 16;                // 16-dim blocks of the PV MFMA
     static constexpr int RS = ROWB + 16;              // LDS row stride of the V tile (padded)
     static constexpr int VTILE = BT * RS;             // bytes of one wave's V tile
-    static constexpr int NB = 4;                      // register ring depth (blocks)
+    static constexpr int NB = PA_RING_DEPTH;          // register ring depth (blocks)
     static_assert(CPR % 4 == 0, "row must split over 4 lane groups");
     static_assert(!FP8 || BT == 32, "fp8 PV uses the k = 32 MFMA");
 };
@@ -108,7 +124,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t *base,
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PA_KV_LOAD_AUX);
 }
 
 // Issue the loads of the block starting at token tb (tb < t1).  A sub-block that

@@ -1,0 +1,72 @@
+// Measurement helpers (libpa_probe.so, not part of the decode path):
+//  * pa_probe_read: streams a buffer once with 16-byte loads and folds it into one
+//    word per workgroup - the HBM read ceiling the decode kernel is compared with;
+//  * pa_probe_copy: plain 16-byte vector copy of a known size - the reference whose
+//    FETCH_SIZE / WRITE_SIZE counter readings calibrate the decode kernel's.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4 *__restrict__ src,
+                                                              size_t n16, uint32_t *__restrict__ sink)
+{
+    const size_t stride = (size_t)gridDim.x * kThreads * kUnroll;
+    uint32_t acc = 0;
+    for (size_t base = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < n16;
+         base += stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const size_t i = base + (size_t)u * kThreads;
+            v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    __shared__ uint32_t red[kThreads];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4 *__restrict__ src,
+                                                              u32x4 *__restrict__ dst, size_t n16)
+{
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// bytes must be a multiple of 16; sink holds `blocks` words.
+int pa_probe_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream)
+{
+    if (!src || !sink || (bytes & 15) || blocks <= 0 || ((uintptr_t)src & 15)) return 1;
+    hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int pa_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream)
+{
+    if (!src || !dst || (bytes & 15) || blocks <= 0 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
+        return 1;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"
