@@ -72,7 +72,8 @@ typedef enum {
 typedef struct {
     int32_t B;                 /* requests (one query token each) */
     int32_t Hkv;               /* KV heads; query heads Hq = Hkv * G */
-    int32_t G;                 /* query heads per KV head (GQA group size; Hkv = 1: MQA) */
+    int32_t G;                 /* query heads per KV head (GQA group size; Hkv = 1: MQA);
+                                  bf16 / fp8: 1..16; MLA: a multiple of 16 up to 128 */
     int32_t D;                 /* q / K head dim: 64 or 128 (bf16, fp8), 576 (MLA) */
     int32_t Dv;                /* V / out head dim: = D, or 512 for MLA */
     int32_t page_size;         /* tokens per page: 16, 32, 64, 128 or 256 */

@@ -57,7 +57,9 @@ pa_status check_desc(const pa_decode_desc *d)
     if ((int64_t)d->max_pages_per_seq * P > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
     if (d->kv_format == PA_KV_MLA656) {
         if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
-        return PA_ERR_UNSUPPORTED;   // no kernel for this format in this build yet
+        if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
+        if (d->s_tok < 656) return PA_ERR_INVALID;
+        return PA_OK;
     }
     if (d->D != d->Dv || (d->D != 64 && d->D != 128)) return PA_ERR_UNSUPPORTED;
     if (d->G > 16) return PA_ERR_UNSUPPORTED;
@@ -78,8 +80,15 @@ pa_status num_parts_for(const pa_decode_desc *d, int *np)
     }
     const int cu = cu_count();
     if (cu <= 0) return PA_ERR_DEVICE;
-    const int wgs_per_cu = 1;
-    int n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
+    int n;
+    if (d->kv_format == PA_KV_MLA656) {
+        // one workgroup per CU over all (part, 64-head group) pairs
+        const int ngroups = (d->G + 63) / 64;
+        n = cu / ngroups;
+    } else {
+        const int wgs_per_cu = 1;
+        n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
+    }
     *np = n < 1 ? 1 : n;
     return PA_OK;
 }
@@ -156,9 +165,10 @@ pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void
     if (!plan || !q || !k_pool || !block_table || !seq_lens || !out || !lse)
         return PA_ERR_INVALID;
     const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
-    if (!v_pool) return PA_ERR_INVALID;
+    const bool mla = desc->kv_format == PA_KV_MLA656;
+    if (mla ? v_pool != nullptr : !v_pool) return PA_ERR_INVALID;
     if (fp8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+    if (!aligned16(q) || !aligned16(k_pool) || (!mla && !aligned16(v_pool)) || !aligned16(out) ||
         ((uintptr_t)lse & 3) || ((uintptr_t)plan & 3) || ((uintptr_t)block_table & 3))
         return PA_ERR_INVALID;
     PlanLayout L;
@@ -200,7 +210,9 @@ pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)desc->D);
     a.scale_log2 = sc * 1.4426950408889634f;
     a.kv_format = desc->kv_format;
-    if (pa::launch_decode(a, (hipStream_t)stream) != hipSuccess) return PA_ERR_DEVICE;
+    const hipError_t e = mla ? pa::launch_mla(a, (hipStream_t)stream)
+                             : pa::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return PA_ERR_DEVICE;
     return PA_OK;
 }
 

@@ -81,6 +81,7 @@ struct DecodeArgs {
 hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout &L,
                        int num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           uint16_t *out, float *lse, int B, int Hkv, int G, int Dv,
                           int chunk_off_off, hipStream_t stream);

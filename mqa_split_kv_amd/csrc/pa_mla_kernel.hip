@@ -1,0 +1,324 @@
+// Split-KV MQA decode over the MLA 656-byte FP8 latent cache (D_qk = 576, D_v = 512,
+// one KV head shared by G query heads, G a multiple of 16 up to 128), gfx950.
+//
+// Token layout (FlashMLA walk-through, section 数据加载, byte-layout table): 512 e4m3
+// codes, 4 fp32 scales (one per 128 codes), 64 bf16 rope values.  The key is the 576
+// dequantised values, the value is their first 512 (V shares the latent with K).
+//
+// One workgroup (4 waves, one per SIMD) = one (part, group of 64 query heads); it walks
+// the part's items.  The two head groups of a part run as workgroups 8 ids apart, i.e.
+// on the same XCD at about the same time, so the second read of each KV tile is an L2
+// hit (the FlashMLA walk-through shares one KV tile between two 64-head CTAs through a
+// cluster, section 计算环节一; here the L2 of the XCD plays that role).  Per 32-token tile:
+//   * raw tile: the 32 tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads into a
+//     3-slot ring (two tiles in flight while one is computed); each wave loads and
+//     later dequantises 8 of the tokens, so it only ever waits for its own loads;
+//   * conversion once per tile (not per head): e4m3 -> bf16 is exact, so the codes go
+//     to a double-buffered bf16 K tile in LDS unscaled, with the token's 4 fp32 tile
+//     scales in the row padding, and the rope values copied (FlashMLA walk-through:
+//     dequantise to bf16 and run bf16 MMA with fp32 accumulation; section 计算环节一
+//     for why dequantisation is the hot spot).  The scales are applied in fp32 instead
+//     of being rounded into the bf16 values: S = sum_t scale_t (q_t . k_t) + q_rope .
+//     k_rope over the four 128-dim tiles t, and for the value dims of tile t the
+//     probabilities are multiplied by scale_t before the PV product;
+//   * each wave owns 16 query heads: S^T[16 tok x 16 heads] = K . Q^T with bf16 MFMA
+//     16x16x32 (K from the LDS tile, Q^T resident in 72 registers), an online softmax
+//     per head column, and O^T[512 x 16 heads] += V^T . P^T with the V^T operand read
+//     back transposed (ds_read_b64_tr_b16) from the same tile; O^T lives in 128
+//     accumulation registers (the register-budget problem the FlashMLA walk-through
+//     describes in section 计算环节二).
+// The running max is only moved when a tile's max exceeds it by more than 2^8, so the
+// 128-register rescale is rare; probabilities stay below 2^8 and the result is the
+// same up to rounding (the reference cancels in the final normalisation).
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define PA_LDS __attribute__((address_space(3)))
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeadsPerWave = 16;
+constexpr int kHeadsPerWG = kWaves * kHeadsPerWave;   // 64
+constexpr int kDqk = 576, kDv = 512;
+constexpr int kTokBytes = 656;
+constexpr int kChunks = kTokBytes / 16;            // 41 16-byte chunks per token
+constexpr int kT = 32;                             // tokens per tile
+constexpr int kTokPerWave = kT / kWaves;           // 8 tokens loaded / dequantised per wave
+constexpr int kWaveChunks = kTokPerWave * kChunks; // 328
+constexpr int kDmaPerWave = (kWaveChunks + 63) / 64;   // 6 direct-to-LDS loads per wave
+constexpr int kRawTile = kT * kTokBytes;           // 20992
+constexpr int kRawSlots = 3;
+constexpr int kKRow = kDqk * 2 + 16;               // bf16 K row stride (padded) = 1168
+constexpr int kKTile = kT * kKRow;                 // 37376
+constexpr int kKSteps = kDqk / 32;                 // 18 (k = 32 per MFMA)
+constexpr int kDvBlocks = kDv / 16;                // 32
+constexpr float kLazyMax = 8.0f;                   // log2 units
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Barrier for LDS handoffs only: this wave's LDS writes are complete, then all waves
+// meet.  (A full __syncthreads would also drain the in-flight KV loads.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4 *)((PA_LDS uint8_t *)p));
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void pa_mla_kernel(
+    DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKTile];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    // workgroup id -> (part, head group): the head groups of one part are 8 ids apart
+    const int wg = blockIdx.x;
+    const int part = (wg / (8 * ngroups)) * 8 + wg % 8;
+    const int group = (wg / 8) % ngroups;
+    if (part >= a.num_parts) return;               // padding of the last id block
+    const int G = a.G, Hq = a.Hkv * a.G;
+    const int head0 = group * kHeadsPerWG + wave * kHeadsPerWave;
+    const bool active = head0 < G;                 // wave-uniform
+    const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
+
+    const int ib = plan[a.part_begin_off + part];
+    const int ie = plan[a.part_begin_off + part + 1];
+
+    for (int it = ib; it < ie; it++) {
+        const int b = plan[a.items_off + 4 * it + 0];
+        const int t0 = plan[a.items_off + 4 * it + 1];
+        const int t1 = plan[a.items_off + 4 * it + 2];
+        const int flags = plan[a.items_off + 4 * it + 3];
+        const int ntiles = (t1 - t0 + kT - 1) / kT;
+
+        // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s
+        auto dma_tile = [&](int j, int s) {
+            const int jc = j < ntiles ? j : ntiles - 1;     // past the end: reload the last tile
+            int tw = t0 + kT * jc + kTokPerWave * wave;     // first of the wave's 8 tokens
+            if (tw >= t1) tw = (t1 - 1) & ~(kTokPerWave - 1);
+            const int page = bt[(int64_t)b * a.max_pages + (tw >> a.page_shift)];
+            const int slot0 = tw & ((1 << a.page_shift) - 1);
+            const uint8_t *src = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot0 * a.s_tok_b;
+            uint8_t *dst = &raw[s][wave * kWaveChunks * 16];
+#pragma unroll
+            for (int i = 0; i < kDmaPerWave; i++) {
+                const int x = 64 * i + lane;
+                if (x < kWaveChunks) {
+                    const int tt = x / kChunks, c = x - tt * kChunks;
+                    __builtin_amdgcn_global_load_lds(src + (int64_t)tt * a.s_tok_b + 16 * c,
+                                                     (PA_LDS void *)(dst + 64 * 16 * i), 16, 0, 0);
+                }
+            }
+        };
+
+        // ---- convert this wave's 8 tokens of raw slot s into K tile buffer kb
+        //      (lane: token tt = lane / 8, latent dims 64p.. of part p = lane % 8, plus rope
+        //      chunk p; lanes with p == 0 also copy the 4 tile scales into the row padding);
+        //      rows of tokens >= t1 become 0 (codes and scales)
+        auto dequant_tile = [&](int j, int s, int kb) {
+            const int tt = lane >> 3, p = lane & 7;
+            const int row = kTokPerWave * wave + tt;
+            const bool valid = t0 + kT * j + row < t1;
+            const uint8_t *tok = &raw[s][row * kTokBytes];
+            uint8_t *dst = &ktile[kb][row * kKRow];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const u32x4 w = *(const u32x4 *)(tok + 64 * p + 16 * c);
+                bf16x8 lo, hi;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
+                    const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
+                    bf16x8 &o = e < 2 ? lo : hi;
+                    const int k = (e & 1) * 4;
+                    o[k + 0] = b0[0];
+                    o[k + 1] = b0[1];
+                    o[k + 2] = b1[0];
+                    o[k + 3] = b1[1];
+                }
+                if (!valid) { lo = bf16x8{}; hi = bf16x8{}; }
+                *(bf16x8 *)(dst + (64 * p + 16 * c) * 2) = lo;
+                *(bf16x8 *)(dst + (64 * p + 16 * c + 8) * 2) = hi;
+            }
+            u32x4 rope = *(const u32x4 *)(tok + 528 + 16 * p);
+            if (!valid) rope = u32x4{0, 0, 0, 0};
+            *(u32x4 *)(dst + (512 + 8 * p) * 2) = rope;
+            if (p == 0) {
+                u32x4 scl = *(const u32x4 *)(tok + 512);
+                if (!valid) scl = u32x4{0, 0, 0, 0};
+                *(u32x4 *)(dst + kDqk * 2) = scl;
+            }
+        };
+
+        // ---- Q^T operand of this wave's 32 heads (B of the 32x32x16 MFMA), resident
+        bf16x8 qop[kKSteps];
+        if (active) {
+            const uint16_t *qrow = a.q + ((int64_t)b * Hq + head0 + col) * kDqk;
+#pragma unroll
+            for (int s = 0; s < kKSteps; s++) qop[s] = *(const bf16x8 *)(qrow + 32 * s + 8 * g4);
+        }
+
+        f32x4 acc[kDvBlocks];
+#pragma unroll
+        for (int i = 0; i < kDvBlocks; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY;     // reference max (log2 domain) of head `col`
+        float l = 0.f;
+
+        if (ntiles > 0) {
+            dma_tile(0, 0);
+            dma_tile(1, 1);
+            wait_vmcnt<kDmaPerWave>();            // own loads of tile 0 done
+            dequant_tile(0, 0, 0);
+            lds_barrier();
+
+            for (int j = 0; j < ntiles; j++) {
+                dma_tile(j + 2, (j + 2) % kRawSlots);
+                const uint8_t *kt = ktile[j & 1];
+
+                if (active) {
+                    // ---- S^T = K . Q^T for the two 16-token row blocks (rows 16sb + 4g4 + r):
+                    //      one partial per 128-dim scale tile (k-steps 4t..4t+3) and one for
+                    //      the rope dims (k-steps 16, 17), combined with the tile scales in fp32
+                    f32x4 st[2];
+                    f32x4 sc4[2][4];       // scales of this lane's 8 tokens: [sb][r] -> 4 tiles
+#pragma unroll
+                    for (int sb = 0; sb < 2; sb++) {
+                        const uint8_t *krow = kt + (16 * sb + col) * kKRow + 16 * g4;
+                        f32x4 part[5];
+#pragma unroll
+                        for (int t = 0; t < 5; t++) {
+                            f32x4 c4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s4 = 0; s4 < (t < 4 ? 4 : 2); s4++) {
+                                const int s = 4 * t + s4;
+                                c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    *(const bf16x8 *)(krow + 64 * s), qop[s], c4, 0, 0, 0);
+                            }
+                            part[t] = c4;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            sc4[sb][r] = *(const f32x4 *)(kt + (16 * sb + 4 * g4 + r) * kKRow + kDqk * 2);
+                            float x = part[4][r];
+#pragma unroll
+                            for (int t = 0; t < 4; t++) x += sc4[sb][r][t] * part[t][r];
+                            st[sb][r] = x;
+                        }
+                    }
+                    // ---- online softmax with a lazily moved reference
+                    float bm = -INFINITY;
+                    float sv[8];
+#pragma unroll
+                    for (int r = 0; r < 8; r++) {
+                        const int tok = t0 + kT * j + 16 * (r >> 2) + 4 * g4 + (r & 3);
+                        sv[r] = tok < t1 ? st[r >> 2][r & 3] * a.scale_log2 : -INFINITY;
+                        bm = fmaxf(bm, sv[r]);
+                    }
+                    bm = fmaxf(bm, __shfl_xor(bm, 16));
+                    bm = fmaxf(bm, __shfl_xor(bm, 32));
+                    if (__any(bm > m + kLazyMax)) {
+                        const float mn = fmaxf(m, bm);
+                        const float alpha = fast_exp2(m - mn);   // m = -inf: 0
+                        m = mn;
+                        l *= alpha;
+#pragma unroll
+                        for (int i = 0; i < kDvBlocks; i++) acc[i] *= alpha;
+                    }
+                    const float mref = m == -INFINITY ? 0.f : m;
+                    bf16x8 pbt[4];         // P times the scale of value tile t, per token
+                    float ps = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 8; r++) {
+                        const float pr = fast_exp2(sv[r] - mref);
+                        ps += pr;
+#pragma unroll
+                        for (int t = 0; t < 4; t++) pbt[t][r] = (__bf16)(pr * sc4[r >> 2][r & 3][t]);
+                    }
+                    l += ps;
+                    // ---- O^T += V^T . P^T; k = 8g4 + r <-> token (r < 4 ? 4g4 + r : 16 + 4g4 + r - 4)
+                    const uint8_t *vbase = kt + (4 * g4 + (col >> 2)) * kKRow + 4 * (col & 3) * 2;
+#pragma unroll
+                    for (int db = 0; db < kDvBlocks; db++) {
+                        const bf16x4 lo = lds_tr16(vbase + 32 * db);
+                        const bf16x4 hi = lds_tr16(vbase + 16 * kKRow + 32 * db);
+                        bf16x8 va;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            va[e] = lo[e];
+                            va[4 + e] = hi[e];
+                        }
+                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbt[db >> 3], acc[db], 0, 0, 0);
+                    }
+                }
+                // ---- next tile: own loads of tile j+1 done (tile j+2's are younger), then
+                //      dequantise it into the other K buffer
+                wait_vmcnt<kDmaPerWave>();
+                dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1);
+                lds_barrier();
+            }
+            wait_vmcnt<0>();
+        }
+
+        // ---- epilogue: this wave's heads are complete for this item
+        if (active) {
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const int head = head0 + col;
+            const bool empty = m == -INFINITY || l == 0.f;
+            const float inv = empty ? 0.f : 1.0f / l;
+            const float lse_v = empty ? -INFINITY : (m + log2f(l)) * 0.69314718055994530942f;
+            const int64_t row = (int64_t)b * Hq + head;
+            // O^T layout: lane holds dims 16db + 4g4 + e of head `col`
+            if (flags & 1) {
+                uint16_t *orow = a.out + row * kDv + 4 * g4;
+#pragma unroll
+                for (int db = 0; db < kDvBlocks; db++) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) o[e] = (__bf16)(acc[db][e] * inv);
+                    *(bf16x4 *)(orow + 16 * db) = o;
+                }
+                if (g4 == 0) a.lse[row] = lse_v;
+            } else {
+                const int64_t prow = (int64_t)it * Hq + head;
+                float *orow = a.ws_o + prow * kDv + 4 * g4;
+#pragma unroll
+                for (int db = 0; db < kDvBlocks; db++) *(f32x4 *)(orow + 16 * db) = acc[db] * inv;
+                if (g4 == 0) a.ws_lse[prow] = lse_v;
+            }
+        }
+        lds_barrier();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream)
+{
+    const int ngroups = (a.G + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int nwg = (a.num_parts + 7) / 8 * 8 * ngroups;
+    hipLaunchKernelGGL(pa_mla_kernel, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
+                       a.block_table, ngroups);
+    return hipGetLastError();
+}
+
+}  // namespace pa

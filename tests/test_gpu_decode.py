@@ -239,3 +239,71 @@ def test_plan_reuse_across_layers():
         out, lse = bf16_bits_to_f64(run.out), run.lse.cpu().numpy().astype(np.float64)
         ref_out, ref_lse = oracle.decode(c)
         assert_parity(c, out, lse, ref_out, ref_lse)
+
+
+# ---------------------------------------------------------------------------- MLA 656-byte
+
+def _mla_case(lens, G=128, P=64, splits=0, pool_extra=2, seed=11):
+    used = sum(-(-L // P) for L in lens)
+    spec = synth.CaseSpec(B=len(lens), Hq=G, Hkv=1, D=576, Dv=512, page_size=P, seq_lens=lens,
+                          kv_format=synth.KV_MLA656, pool_pages=used + pool_extra,
+                          num_splits=splits)
+    return synth.make_case(spec, seed)
+
+
+MLA_SMALL = [
+    dict(lens=(300, 1, 64)),
+    dict(lens=(300, 1, 64), splits=1),
+    dict(lens=(1000, 33), splits=3),
+    dict(lens=(129, 2000), G=64, P=16),
+    dict(lens=(31, 32, 33), G=16, P=32, splits=2),
+    dict(lens=(0, 100, 0)),
+]
+
+
+@pytest.mark.parametrize("kw", MLA_SMALL)
+def test_mla_small_parity(kw):
+    case = _mla_case(**kw)
+    out, lse = GpuRun(case)()
+    ref_out, ref_lse = oracle.decode(case)
+    assert_parity(case, out, lse, ref_out, ref_lse)
+
+
+def test_mla_config_full_sampled():
+    case = synth.config_case(4)
+    run = GpuRun(case)
+    out, lse = run()
+    B = case["B"]
+    pairs = np.zeros((B, 1), bool)
+    pairs[[0, 17, 40, B - 1], 0] = True
+    ref_out, ref_lse = oracle.decode(case, pairs=pairs)
+    rows = np.repeat(pairs, case["G"], axis=1)
+    assert_parity(case, out, lse, ref_out, ref_lse, rows=rows)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_mla_needle(splits):
+    lens = (257, 96)
+    case = _mla_case(lens, G=32, P=64, splits=splits)
+    rng = np.random.default_rng(2)
+    targets = {0: 256, 1: 31}
+    for b, t in targets.items():
+        u = rng.standard_normal(576).astype(np.float32)
+        u /= np.linalg.norm(u)
+        case["q"][b] = synth.f32_to_bf16_bits(np.tile(u * 4.0, (case["G"], 1)))
+        page = case["block_table"][b, t // 64]
+        x = (u * 12.0).astype(np.float32)
+        nope = x[:512].reshape(4, 128)
+        sc = (np.abs(nope).max(-1) / np.float32(448.0)).astype(np.float32)
+        tok = case["k_pool"][page, t % 64]
+        tok[:512] = synth.f32_to_e4m3_codes(nope / sc[:, None]).reshape(512)
+        tok[512:528] = sc.view(np.uint8)
+        tok[528:] = synth.f32_to_bf16_bits(x[512:]).view(np.uint8)
+    scale = 8.0 / math.sqrt(576)          # needle logit ~16 vs spread ~1.3: weight of the rest < 1e-3
+    out, lse = GpuRun(case)(scale=scale)
+    ref_out, ref_lse = oracle.decode(case, scale=scale)
+    assert_parity(case, out, lse, ref_out, ref_lse)
+    for b, t in targets.items():
+        v = oracle.mla656_unpack(case["k_pool"][case["block_table"][b, t // 64], t % 64])[:512]
+        np.testing.assert_allclose(out[b], np.tile(v, (case["G"], 1)), atol=0.05)
