@@ -100,6 +100,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const bool active = head0 < G;                 // wave-uniform
     const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
 
+    // lane byte offset of chunk x = 64 i + lane (token x / 41, chunk x % 41) inside the
+    // 8 token rows a wave loads per tile
+    int dma_off[kDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; i++) {
+        const int x = 64 * i + lane;
+        const int tt = x / kChunks, c = x - tt * kChunks;
+        dma_off[i] = tt * (int)a.s_tok_b + 16 * c;
+    }
+
     const int ib = plan[a.part_begin_off + part];
     const int ie = plan[a.part_begin_off + part + 1];
 
@@ -110,62 +120,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int flags = plan[a.items_off + 4 * it + 3];
         const int ntiles = (t1 - t0 + kT - 1) / kT;
 
-        // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s
+        // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s (buffer
+        //      loads over the 8 token rows: one 32-bit lane offset per instruction)
         auto dma_tile = [&](int j, int s) {
             const int jc = j < ntiles ? j : ntiles - 1;     // past the end: reload the last tile
             int tw = t0 + kT * jc + kTokPerWave * wave;     // first of the wave's 8 tokens
             if (tw >= t1) tw = (t1 - 1) & ~(kTokPerWave - 1);
             const int page = bt[(int64_t)b * a.max_pages + (tw >> a.page_shift)];
             const int slot0 = tw & ((1 << a.page_shift) - 1);
-            const uint8_t *src = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot0 * a.s_tok_b;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot0 * a.s_tok_b), (short)0,
+                kTokPerWave * (int)a.s_tok_b, 0x00020000);
             uint8_t *dst = &raw[s][wave * kWaveChunks * 16];
 #pragma unroll
             for (int i = 0; i < kDmaPerWave; i++) {
-                const int x = 64 * i + lane;
-                if (x < kWaveChunks) {
-                    const int tt = x / kChunks, c = x - tt * kChunks;
-                    __builtin_amdgcn_global_load_lds(src + (int64_t)tt * a.s_tok_b + 16 * c,
-                                                     (PA_LDS void *)(dst + 64 * 16 * i), 16, 0, 0);
-                }
+                if (64 * i + lane < kWaveChunks)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void *)(dst + 64 * 16 * i), 16,
+                                                             dma_off[i], 0, 0, 0);
             }
         };
 
-        // ---- convert this wave's 8 tokens of raw slot s into K tile buffer kb
-        //      (lane: token tt = lane / 8, latent dims 64p.. of part p = lane % 8, plus rope
-        //      chunk p; lanes with p == 0 also copy the 4 tile scales into the row padding);
-        //      rows of tokens >= t1 become 0 (codes and scales)
+        // ---- convert this wave's 8 tokens of raw slot s into K tile buffer kb.  Lane l
+        //      converts latent dims 8l..8l+7 of one token per round (8-byte reads, 16-byte
+        //      writes: 16 neighbouring lanes touch 256 contiguous bytes, no bank conflicts);
+        //      then the rope chunks (lane: token l / 8, chunk l % 8) and the 4 tile scales
+        //      (lanes 0-7, into the row padding).  Rows of tokens >= t1 become 0.
         auto dequant_tile = [&](int j, int s, int kb) {
-            const int tt = lane >> 3, p = lane & 7;
-            const int row = kTokPerWave * wave + tt;
-            const bool valid = t0 + kT * j + row < t1;
-            const uint8_t *tok = &raw[s][row * kTokBytes];
-            uint8_t *dst = &ktile[kb][row * kKRow];
+            const int row0 = kTokPerWave * wave;
+            const int tbase = t0 + kT * j + row0;
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const u32x4 w = *(const u32x4 *)(tok + 64 * p + 16 * c);
-                bf16x8 lo, hi;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false);
-                    const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true);
-                    bf16x8 &o = e < 2 ? lo : hi;
-                    const int k = (e & 1) * 4;
-                    o[k + 0] = b0[0];
-                    o[k + 1] = b0[1];
-                    o[k + 2] = b1[0];
-                    o[k + 3] = b1[1];
-                }
-                if (!valid) { lo = bf16x8{}; hi = bf16x8{}; }
-                *(bf16x8 *)(dst + (64 * p + 16 * c) * 2) = lo;
-                *(bf16x8 *)(dst + (64 * p + 16 * c + 8) * 2) = hi;
+            for (int tt = 0; tt < kTokPerWave; tt++) {
+                const uint8_t *tok = &raw[s][(row0 + tt) * kTokBytes];
+                const uint2 w = *(const uint2 *)(tok + 8 * lane);
+                bf16x8 o;
+                const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+                const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+                const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+                const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+                o[0] = b0[0]; o[1] = b0[1]; o[2] = b1[0]; o[3] = b1[1];
+                o[4] = b2[0]; o[5] = b2[1]; o[6] = b3[0]; o[7] = b3[1];
+                if (tbase + tt >= t1) o = bf16x8{};
+                *(bf16x8 *)(&ktile[kb][(row0 + tt) * kKRow + 16 * lane]) = o;
             }
-            u32x4 rope = *(const u32x4 *)(tok + 528 + 16 * p);
-            if (!valid) rope = u32x4{0, 0, 0, 0};
-            *(u32x4 *)(dst + (512 + 8 * p) * 2) = rope;
-            if (p == 0) {
+            {
+                const int tt = lane >> 3, c = lane & 7;
+                const uint8_t *tok = &raw[s][(row0 + tt) * kTokBytes];
+                u32x4 rope = *(const u32x4 *)(tok + 528 + 16 * c);
+                if (tbase + tt >= t1) rope = u32x4{0, 0, 0, 0};
+                *(u32x4 *)(&ktile[kb][(row0 + tt) * kKRow + (512 + 8 * c) * 2]) = rope;
+            }
+            if (lane < kTokPerWave) {
+                const uint8_t *tok = &raw[s][(row0 + lane) * kTokBytes];
                 u32x4 scl = *(const u32x4 *)(tok + 512);
-                if (!valid) scl = u32x4{0, 0, 0, 0};
-                *(u32x4 *)(dst + kDqk * 2) = scl;
+                if (tbase + lane >= t1) scl = u32x4{0, 0, 0, 0};
+                *(u32x4 *)(&ktile[kb][(row0 + lane) * kKRow + kDqk * 2]) = scl;
             }
         };
 
@@ -190,30 +198,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             dequant_tile(0, 0, 0);
             lds_barrier();
 
-            for (int j = 0; j < ntiles; j++) {
-                dma_tile(j + 2, (j + 2) % kRawSlots);
+            // The tile loop never rescales O^T itself: when a tile's max exceeds the
+            // reference by more than 2^8 it leaves (before that tile's PV), the rescale
+            // runs outside, and the loop resumes at the same tile.  Inside the loop O^T is
+            // only touched by MFMAs, so it stays in the accumulation registers.
+            int j = 0;
+            int dma_next = 2;                     // next tile whose loads are not issued yet
+            float bm_exit = -INFINITY;
+            for (;;) {
+            for (; j < ntiles; j++) {
+                // tile j+2's loads go out before the compute of tile j (once per tile, also
+                // when the loop resumes at j after a rescale)
+                if (dma_next == j + 2) {
+                    dma_tile(j + 2, (j + 2) % kRawSlots);
+                    dma_next++;
+                }
                 const uint8_t *kt = ktile[j & 1];
 
                 if (active) {
                     // ---- S^T = K . Q^T for the two 16-token row blocks (rows 16sb + 4g4 + r):
                     //      one partial per 128-dim scale tile (k-steps 4t..4t+3) and one for
                     //      the rope dims (k-steps 16, 17), combined with the tile scales in fp32
+                    // Per 16-token row block: 18 MFMA steps whose K operand is read from LDS
+                    // two steps ahead; the scheduling barriers pin that order (one wave per
+                    // SIMD: nothing else hides the LDS latency).
                     f32x4 st[2];
                     f32x4 sc4[2][4];       // scales of this lane's 8 tokens: [sb][r] -> 4 tiles
 #pragma unroll
                     for (int sb = 0; sb < 2; sb++) {
-                        const uint8_t *krow = kt + (16 * sb + col) * kKRow + 16 * g4;
                         f32x4 part[5];
 #pragma unroll
-                        for (int t = 0; t < 5; t++) {
-                            f32x4 c4 = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int t = 0; t < 5; t++) part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        const uint8_t *kbase = kt + (16 * sb + col) * kKRow + 16 * g4;
+                        bf16x8 kf[3];
+                        kf[0] = *(const bf16x8 *)kbase;
+                        kf[1] = *(const bf16x8 *)(kbase + 64);
 #pragma unroll
-                            for (int s4 = 0; s4 < (t < 4 ? 4 : 2); s4++) {
-                                const int s = 4 * t + s4;
-                                c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    *(const bf16x8 *)(krow + 64 * s), qop[s], c4, 0, 0, 0);
-                            }
-                            part[t] = c4;
+                        for (int ks = 0; ks < kKSteps; ks++) {
+                            if (ks + 2 < kKSteps) kf[(ks + 2) % 3] = *(const bf16x8 *)(kbase + 64 * (ks + 2));
+                            const int t = ks < 16 ? ks / 4 : 4;
+                            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3], qop[ks], part[t], 0, 0, 0);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
@@ -236,12 +261,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     bm = fmaxf(bm, __shfl_xor(bm, 16));
                     bm = fmaxf(bm, __shfl_xor(bm, 32));
                     if (__any(bm > m + kLazyMax)) {
-                        const float mn = fmaxf(m, bm);
-                        const float alpha = fast_exp2(m - mn);   // m = -inf: 0
-                        m = mn;
-                        l *= alpha;
-#pragma unroll
-                        for (int i = 0; i < kDvBlocks; i++) acc[i] *= alpha;
+                        bm_exit = bm;
+                        break;
                     }
                     const float mref = m == -INFINITY ? 0.f : m;
                     bf16x8 pbt[4];         // P times the scale of value tile t, per token
@@ -256,8 +277,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     l += ps;
                     // ---- O^T += V^T . P^T; k = 8g4 + r <-> token (r < 4 ? 4g4 + r : 16 + 4g4 + r - 4)
                     const uint8_t *vbase = kt + (4 * g4 + (col >> 2)) * kKRow + 4 * (col & 3) * 2;
-#pragma unroll
-                    for (int db = 0; db < kDvBlocks; db++) {
+                    auto read_vt = [&](int db) {
                         const bf16x4 lo = lds_tr16(vbase + 32 * db);
                         const bf16x4 hi = lds_tr16(vbase + 16 * kKRow + 32 * db);
                         bf16x8 va;
@@ -266,7 +286,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                             va[e] = lo[e];
                             va[4 + e] = hi[e];
                         }
-                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbt[db >> 3], acc[db], 0, 0, 0);
+                        return va;
+                    };
+                    bf16x8 vf[3];
+                    vf[0] = read_vt(0);
+                    vf[1] = read_vt(1);
+#pragma unroll
+                    for (int db = 0; db < kDvBlocks; db++) {
+                        if (db + 2 < kDvBlocks) vf[(db + 2) % 3] = read_vt(db + 2);
+                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db % 3], pbt[db >> 3], acc[db], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
                 // ---- next tile: own loads of tile j+1 done (tile j+2's are younger), then
@@ -274,6 +303,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 wait_vmcnt<kDmaPerWave>();
                 dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1);
                 lds_barrier();
+            }
+            if (j >= ntiles) break;
+            // move the reference to this tile's max and rescale (rare); tile j is redone
+            {
+                const float mn = fmaxf(m, bm_exit);
+                const float alpha = fast_exp2(m - mn);   // m = -inf: 0
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int i = 0; i < kDvBlocks; i++) acc[i] *= alpha;
+            }
             }
             wait_vmcnt<0>();
         }
