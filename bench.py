@@ -22,6 +22,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MLA_FLOP_PER_TOKEN = 2 * 128 * (576 + 512)   # q.k over 576 dims and p.v over 512, 128 heads
+
+
+def counter_traffic(workload):
+    """Calibrated HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings, or None when the kernel source has
+    changed since they were taken (or none were taken for this workload)."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+        w = rec["workloads"][workload]
+        with open(os.path.join(ROOT, w["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != w["source_sha256"]:
+                return None
+        return int(round(w["fetch_kib"] * 1024 * rec["fetch_factor"]
+                         + w["write_kib"] * 1024 * rec["write_factor"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -33,15 +53,16 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="batch of the HD64 workload (1 or 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--graph", action="store_true", help="also time hipGraph replay of a step")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
     return ap.parse_args()
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the split-KV path shards by request / KV head without any exchange, see DESIGN.md",
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the path would "
+              "shard by request or KV head with no exchange, or by sequence with an all-gather "
+              "of the (O, lse) partials before the same combine kernel",
               file=sys.stderr)
         sys.exit(2)
 
@@ -120,7 +141,7 @@ def main():
     torch.cuda.synchronize()
 
     graph_us = None
-    if args.graph:
+    if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -147,6 +168,19 @@ def main():
     gbs = kv_bytes / (step_us * 1e-6) / 1e9
     dec_gbs = kv_bytes / (decode_us * 1e-6) / 1e9
     fmt = {0: "bf16", 1: "fp8e4m3-kv/bf16", 2: "mla656-fp8/bf16"}[case["kv_format"]]
+
+    traffic = counter_traffic(case["name"])
+    if case["kv_format"] == 2:
+        # MLA: 128 heads share each token, so the contraction is MFMA-bound
+        tflops = MLA_FLOP_PER_TOKEN * float(np.sum(case["seq_lens"])) / (decode_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "pa_mla_kernel"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "pa_decode_kernel<%d,%s>" % (case["D"], "bf16" if case["kv_format"] == 0 else "fp8")}
+    roof["algorithmic_bytes"] = kv_bytes
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -178,8 +212,7 @@ def main():
         "decode_kernel_us": round(decode_us, 2),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
         "wall_s_timed": round(wall_s, 4),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
