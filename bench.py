@@ -2,9 +2,9 @@
 """Benchmark: paged split-KV GQA decode attention on one MI355X.
 
 One step = pa_decode_run + pa_decode_combine (split-KV decode kernel + combine
-kernel) over the whole batch, on one stream, with every input resident in HBM; the
-plan is built once before timing (it is reusable while lengths are unchanged) and
-timed separately.  Default workload: GQA decode at a Llama-70B-like shape (B=32,
+kernel) over the whole batch, on one stream, with every input resident in HBM
+(--fused-combine merges inside the decode kernel instead).  The plan is built once
+before timing (it is reusable while lengths are unchanged) and timed separately.  Default workload: GQA decode at a Llama-70B-like shape (B=32,
 Hq=64, Hkv=8, D=128, bf16 KV, 64-token pages, 4096 tokens each, balanced plan).
 
 Prints ONE JSON line.  `value` is the achieved algorithmic KV bandwidth (GB/s) of a
@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="merge chunks inside the decode kernel (last workgroup per request) "
+                         "instead of the combine kernel")
     return ap.parse_args()
 
 
@@ -93,7 +96,7 @@ def main():
     B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
     out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    desc = pb.desc_from_case(case)
+    desc = pb.desc_from_case(case, fused=args.fused_combine)
     runner = pb.PagedDecode(desc)
     stream = torch.cuda.current_stream()
 
@@ -142,6 +145,9 @@ def main():
 
     graph_us = None
     if not args.no_graph:
+        # several steps per graph, so that the per-replay launch cost is amortised and
+        # the figure is the device time of a step
+        per_graph = 20
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -150,17 +156,19 @@ def main():
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step()
-        for _ in range(10):
+            for _ in range(per_graph):
+                step()
+        for _ in range(2):
             g.replay()
         torch.cuda.synchronize()
+        reps = max(1, args.steps // per_graph)
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(args.steps):
+        for _ in range(reps):
             g.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1000.0 / args.steps
+        graph_us = g0.elapsed_time(g1) * 1000.0 / (reps * per_graph)
 
     kv_bytes = synth.kv_bytes(case)
     io = synth.io_bytes(case)
@@ -189,7 +197,9 @@ def main():
     cfg = {"workload": case["name"], "B": B, "Hq": Hq, "Hkv": case["Hkv"], "D": case["D"],
            "Dv": Dv, "page_size": case["page_size"], "seq_len_total": int(np.sum(case["seq_lens"])),
            "kv_format": fmt, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
-           "num_parts": pb.pa_decode_num_parts(desc), "parallelism": "single GPU"}
+           "num_parts": pb.pa_decode_num_parts(desc),
+           "combine": "fused in the decode kernel" if args.fused_combine else "combine kernel",
+           "parallelism": "single GPU"}
     rec = {
         "metric": "decode-attention µs/step + achieved KV HBM GB/s (% of MI355X peak)",
         "value": round(gbs, 1),

@@ -28,6 +28,16 @@
  *                      in one chunk, partials (workspace) for the others
  *   pa_decode_combine  LSE-weighted merge of the partials into out / lse
  *
+ * With PA_FLAG_FUSED_COMBINE (bf16 and fp8 page-head formats) the merge runs inside
+ * pa_decode_run instead: the workgroup that finishes the last chunk of a request
+ * merges that request's chunks (the XQA article's "last CTA merges" variant, section
+ * "归约怎么记"), found with a device-scope counter per (request, row group) kept in
+ * the plan buffer; then pa_decode_combine has nothing to do and returns without
+ * launching.  On MI355X this is slower than the separate combine kernel: the
+ * device-scope release that publishes the partials writes back the L2 of the
+ * workgroup's XCD (the 8 XCD caches are not coherent with each other), which costs
+ * more than the combine launch it saves.
+ *
  * Ownership: the caller allocates and owns every buffer (device memory for all
  * array arguments).  The library never allocates, frees or synchronises; it keeps
  * no state except a per-device compute-unit count.  Calls on one stream are
@@ -69,6 +79,12 @@ typedef enum {
     PA_KV_MLA656 = 2
 } pa_kv_format;
 
+enum {
+    /* pa_decode_run merges the chunks itself; pa_decode_combine becomes a no-op.
+       Not for PA_KV_MLA656 (PA_ERR_UNSUPPORTED). */
+    PA_FLAG_FUSED_COMBINE = 1
+};
+
 typedef struct {
     int32_t B;                 /* requests (one query token each) */
     int32_t Hkv;               /* KV heads; query heads Hq = Hkv * G */
@@ -90,7 +106,7 @@ typedef struct {
     int32_t q_len;             /* query tokens per request: must be 1 */
     int32_t num_splits;        /* 0: balanced split scheduling; s > 0: s chunks per request */
     int32_t kv_format;         /* pa_kv_format */
-    int32_t reserved;          /* must be 0 */
+    int32_t flags;             /* 0 or PA_FLAG_FUSED_COMBINE; other bits: PA_ERR_INVALID */
 } pa_decode_desc;
 
 /*
@@ -107,7 +123,9 @@ typedef struct {
  * unit (FlashMLA walk-through, section 调度); a request is cut where a part ends.
  *
  * The plan stays valid while the desc and seq_lens are unchanged, so one plan can
- * serve every layer of a decode step.
+ * serve every layer of a decode step.  The plan's last words are the fused-combine
+ * counters (B x row groups, a row group being the G query heads of one KV head, or 64
+ * query heads for PA_KV_MLA656); the plan kernel zeroes them.
  */
 pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, void *plan,
                          size_t *plan_bytes, size_t *workspace_bytes, void *stream);
@@ -122,12 +140,16 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
  *               the plan was built from)
  *   scale       logit scale; <= 0 selects 1/sqrt(D)
  *   out         [B][Hq][Dv] bf16; lse [B][Hq] fp32 (natural log)
- *   plan        written by pa_decode_plan for the same desc
+ *   plan        written by pa_decode_plan for the same desc (flags may differ).  With
+ *               PA_FLAG_FUSED_COMBINE the kernel counts finished chunks in the plan's
+ *               counter words and leaves them at zero when it completes, so runs that
+ *               share one plan must be ordered (one stream), never concurrent.
  *   workspace   >= the size pa_decode_plan reported (fp32 partials), 16-byte aligned
- * Rows of requests that the plan cuts into several chunks are only complete after
- * pa_decode_combine.
+ * Without PA_FLAG_FUSED_COMBINE, rows of requests that the plan cuts into several
+ * chunks (and rows of length-0 requests under the balanced rule) are only complete
+ * after pa_decode_combine; with it, every row is complete when the kernel ends.
  */
-pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void *q,
+pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
                         const void *k_pool, const void *v_pool, const float *k_scale,
                         const float *v_scale, const int32_t *block_table,
                         const int32_t *seq_lens, float scale, void *out, float *lse,
@@ -138,7 +160,8 @@ pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void
  * 0) merges the chunk partials: M = max_i lse_i, lse = M + ln sum_i exp(lse_i - M),
  * out = sum_i exp(lse_i - lse) * O_i (XQA article, section "归约怎么记", merge
  * equation, written for normalised partials).  Requests done in one chunk are left
- * as pa_decode_run wrote them.  A no-op launch-free call when num_splits == 1.
+ * as pa_decode_run wrote them.  A no-op launch-free call when num_splits == 1 or the
+ * desc has PA_FLAG_FUSED_COMBINE.
  */
 pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
                             void *out, float *lse, void *stream);

@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_SIZE, PA_ERR_DEVICE = range(5)
 PA_KV_BF16, PA_KV_FP8_E4M3_PAGE_HEAD, PA_KV_MLA656 = range(3)
+PA_FLAG_FUSED_COMBINE = 1
 EXPORTS = ("pa_decode_plan", "pa_decode_run", "pa_decode_combine", "pa_decode_num_parts",
            "pa_status_string")
 
@@ -29,7 +30,7 @@ class PaDecodeDesc(ctypes.Structure):
         ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("s_page", ctypes.c_int64), ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64),
         ("q_len", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-        ("kv_format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -68,17 +69,19 @@ def status_string(s: int) -> str:
 
 
 def make_desc(B, Hkv, G, D, Dv, page_size, num_pages, max_pages_per_seq, s_page, s_head,
-              s_tok, num_splits=0, kv_format=PA_KV_BF16, q_len=1) -> PaDecodeDesc:
+              s_tok, num_splits=0, kv_format=PA_KV_BF16, q_len=1, flags=0) -> PaDecodeDesc:
     return PaDecodeDesc(B, Hkv, G, D, Dv, page_size, num_pages, max_pages_per_seq, s_page,
-                        s_head, s_tok, q_len, num_splits, kv_format, 0)
+                        s_head, s_tok, q_len, num_splits, kv_format, flags)
 
 
-def desc_from_case(case: dict, num_splits: Optional[int] = None) -> PaDecodeDesc:
+def desc_from_case(case: dict, num_splits: Optional[int] = None, fused: bool = False,
+                   q_len: int = 1) -> PaDecodeDesc:
     """Descriptor for an instance drawn by ``mqa_split_kv_amd.synth``."""
     ns = case["num_splits"] if num_splits is None else num_splits
     return make_desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
                      case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
-                     case["s_tok"], ns, case["kv_format"])
+                     case["s_tok"], ns, case["kv_format"], q_len=q_len,
+                     flags=PA_FLAG_FUSED_COMBINE if fused else 0)
 
 
 def _p(t):

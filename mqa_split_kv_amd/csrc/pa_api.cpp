@@ -42,7 +42,8 @@ pa_status check_desc(const pa_decode_desc *d)
     if (d->B <= 0 || d->Hkv <= 0 || d->G <= 0 || d->D <= 0 || d->Dv <= 0) return PA_ERR_INVALID;
     if (d->page_size <= 0 || d->num_pages <= 0 || d->max_pages_per_seq <= 0) return PA_ERR_INVALID;
     if (d->s_page < 0 || d->s_head < 0 || d->s_tok <= 0) return PA_ERR_INVALID;
-    if (d->num_splits < 0 || d->reserved != 0 || d->q_len <= 0) return PA_ERR_INVALID;
+    if (d->num_splits < 0 || (d->flags & ~(int32_t)PA_FLAG_FUSED_COMBINE) != 0 || d->q_len <= 0)
+        return PA_ERR_INVALID;
     if (d->kv_format != PA_KV_BF16 && d->kv_format != PA_KV_FP8_E4M3_PAGE_HEAD &&
         d->kv_format != PA_KV_MLA656)
         return PA_ERR_INVALID;
@@ -56,6 +57,9 @@ pa_status check_desc(const pa_decode_desc *d)
     if (d->num_splits > 256) return PA_ERR_UNSUPPORTED;
     if ((int64_t)d->max_pages_per_seq * P > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
     if (d->kv_format == PA_KV_MLA656) {
+        // the MLA kernel keeps its whole register file for the tile loop; its chunks are
+        // merged by the combine kernel only
+        if (d->flags & PA_FLAG_FUSED_COMBINE) return PA_ERR_UNSUPPORTED;
         if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
         if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
         if (d->s_tok < 656) return PA_ERR_INVALID;
@@ -98,7 +102,8 @@ pa_status layout_for(const pa_decode_desc *d, PlanLayout *L)
     int np = 0;
     pa_status st = num_parts_for(d, &np);
     if (st != PA_OK) return st;
-    *L = pa::plan_layout(d->B, d->num_splits, np);
+    const int rowgroups = d->kv_format == PA_KV_MLA656 ? (d->G + 63) / 64 : d->Hkv;
+    *L = pa::plan_layout(d->B, rowgroups, d->num_splits, np);
     return PA_OK;
 }
 
@@ -154,7 +159,7 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
     return PA_OK;
 }
 
-pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void *q,
+pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
                         const void *k_pool, const void *v_pool, const float *k_scale,
                         const float *v_scale, const int32_t *block_table,
                         const int32_t *seq_lens, float scale, void *out, float *lse,
@@ -207,6 +212,10 @@ pa_status pa_decode_run(const pa_decode_desc *desc, const void *plan, const void
     a.num_parts = L.num_parts;
     a.part_begin_off = L.part_begin_off;
     a.items_off = L.items_off;
+    a.chunk_off_off = L.chunk_off_off;
+    a.counters = (desc->flags & PA_FLAG_FUSED_COMBINE) && desc->num_splits != 1
+                     ? (int32_t *)plan + L.counters_off
+                     : nullptr;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)desc->D);
     a.scale_log2 = sc * 1.4426950408889634f;
     a.kv_format = desc->kv_format;
@@ -223,6 +232,7 @@ pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const 
     if (st != PA_OK) return st;
     if (!plan || !out || !lse) return PA_ERR_INVALID;
     if (desc->num_splits == 1) return PA_OK;     // every request is a single chunk
+    if (desc->flags & PA_FLAG_FUSED_COMBINE) return PA_OK;   // pa_decode_run merged
     if (!workspace || !aligned16(workspace) || !aligned16(out) || ((uintptr_t)lse & 3))
         return PA_ERR_INVALID;
     PlanLayout L;

@@ -25,7 +25,7 @@
 // FP8 K/V are converted to bf16 exactly in registers; the K scale of a page
 // multiplies that page's logits, the V scale multiplies P before the PV product
 // (XQA article, section "FP8 / INT8 的 KV: 转换到底放在哪儿", scale folding).
-#include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
     __shared__ float s_M[16], s_L[16];
+    __shared__ int s_flag;
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -434,6 +435,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         __syncthreads();
     }
+    // fused combine: the last workgroup to finish a request's chunks merges them
+    if (a.counters) fused_combine_tail(a, plan, part, ib, ie, h, a.Hkv, h * G, G, &s_flag);
 }
 
 }  // namespace

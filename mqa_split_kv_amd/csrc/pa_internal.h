@@ -21,7 +21,11 @@ constexpr int kMaxBatch = 4096;       // plan kernel keeps per-request prefix su
 //   [0] magic  [1] mode (0 fixed splits, 1 balanced)  [2] B  [3] num_parts
 //   [4] num_items  [5] tile tokens  [6] max_items  [7] 0
 //   part_begin[num_parts + 1] | chunk_off[B + 1] | items[max_items][4] = {b, tok0, tok1, flags}
+//   | counters[B][n_rowgroups]
 //   flags bit 0: the item is its request's only chunk and writes the final row.
+//   counters: chunks of (request, row group) finished so far in a fused-combine run;
+//   zeroed by the plan kernel, returned to zero by the run that uses them.  A row group
+//   is the G query rows of one KV head (bf16 / fp8) or one 64-head group (MLA).
 struct PlanLayout {
     int mode;
     int B;
@@ -30,10 +34,12 @@ struct PlanLayout {
     int part_begin_off;
     int chunk_off_off;
     int items_off;
+    int counters_off;
+    int n_counters;
     size_t words;
 };
 
-inline PlanLayout plan_layout(int B, int num_splits, int num_parts)
+inline PlanLayout plan_layout(int B, int n_rowgroups, int num_splits, int num_parts)
 {
     PlanLayout L;
     L.mode = num_splits > 0 ? 0 : 1;
@@ -43,7 +49,9 @@ inline PlanLayout plan_layout(int B, int num_splits, int num_parts)
     L.part_begin_off = kPlanHeaderWords;
     L.chunk_off_off = L.part_begin_off + num_parts + 1;
     L.items_off = L.chunk_off_off + B + 1;
-    L.words = (size_t)L.items_off + 4 * (size_t)L.max_items;
+    L.counters_off = L.items_off + 4 * L.max_items;
+    L.n_counters = B * n_rowgroups;
+    L.words = (size_t)L.counters_off + (size_t)L.n_counters;
     return L;
 }
 
@@ -73,7 +81,8 @@ struct DecodeArgs {
     float *ws_lse;
     int64_t s_page_b, s_head_b, s_tok_b;   // pool strides in bytes
     int B, Hkv, G, D, Dv, max_pages, page_shift;
-    int num_parts, part_begin_off, items_off;
+    int num_parts, part_begin_off, items_off, chunk_off_off;
+    int32_t *counters;          // plan counter words; non-null: fused combine
     float scale_log2;           // logit scale * log2(e)
     int kv_format;
 };

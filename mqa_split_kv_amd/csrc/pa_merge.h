@@ -1,0 +1,150 @@
+// Device-side LSE merge of chunk partials, used by the combine kernel and by the
+// fused-combine epilogue of the decode kernels (the last workgroup to finish a
+// request's chunks merges them).  XQA article, section "归约怎么记", merge equation,
+// written for normalised partials O_i with natural-log lse_i:
+//   M = max_i lse_i,  lse = M + ln sum_i exp(lse_i - M),  out = sum_i exp(lse_i - lse) O_i.
+// Chunks with lse_i = -inf (empty ranges) carry no weight; rows with no non-empty chunk
+// get out = 0 and lse = -inf, without forming -inf - (-inf) (pipelining page, section 三).
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 merge_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
+
+// Partial row of query head hq in chunk c: ws_o[(c * Hq + hq) * Dv ...], ws_lse[c * Hq + hq].
+// Merges query heads [hq0, hq0 + nrows) of request b from chunks c0 .. c0 + n - 1.  A work
+// unit is one head and 4 dims; thread tid takes units tid, tid + nthr, ... kUnits at a
+// time (1 in the wide combine grid, 4 in a single fused-combine workgroup), and reads the
+// chunks kChunkBatch at a time with a running maximum (the same rescaling as the online
+// softmax), so that up to kUnits x kChunkBatch partial loads are in flight instead of one
+// dependent load after another.  A unit's arithmetic does not depend on kUnits, so both
+// callers produce the same bits.  The result is
+//   out = sum_i exp(lse_i - M) O_i / sum_i exp(lse_i - M),  lse = M + ln sum_i exp(lse_i - M)
+// which is the merge equation above with exp(lse_i - lse) = exp(lse_i - M) / sum.
+constexpr int kChunkBatch = 4;
+
+template <int kUnits>
+__device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16_t *out,
+                                  float *lse, int b, int64_t c0, int n, int Hq, int Dv, int hq0,
+                                  int nrows, int tid, int nthr)
+{
+    const int q4 = Dv / 4;
+    const int total = nrows * q4;
+    for (int u0 = tid; u0 < total; u0 += kUnits * nthr) {
+        int64_t prow0[kUnits];
+        bool ok[kUnits];
+        float m[kUnits], s[kUnits];
+        merge_f32x4 acc[kUnits];
+#pragma unroll
+        for (int j = 0; j < kUnits; j++) {
+            const int u = u0 + j * nthr;
+            ok[j] = u < total;
+            const int hq = hq0 + (ok[j] ? u / q4 : 0);
+            prow0[j] = c0 * Hq + hq;
+            m[j] = -INFINITY;
+            s[j] = 0.f;
+            acc[j] = merge_f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int i0 = 0; i0 < n; i0 += kChunkBatch) {
+            float lv[kUnits][kChunkBatch];
+            merge_f32x4 ov[kUnits][kChunkBatch];
+#pragma unroll
+            for (int j = 0; j < kUnits; j++) {
+                const int d0 = ((u0 + j * nthr) % q4) * 4;
+#pragma unroll
+                for (int k = 0; k < kChunkBatch; k++) {
+                    const bool in = ok[j] && i0 + k < n;
+                    const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hq;
+                    lv[j][k] = in ? ws_lse[prow] : -INFINITY;
+                    ov[j][k] = in ? *(const merge_f32x4 *)(ws_o + prow * Dv + d0)
+                                  : merge_f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kUnits; j++) {
+                float mb = m[j];
+#pragma unroll
+                for (int k = 0; k < kChunkBatch; k++) mb = fmaxf(mb, lv[j][k]);
+                if (mb == -INFINITY) continue;            // nothing non-empty yet
+                const float alpha = expf(m[j] - mb);      // m = -inf: 0
+                s[j] *= alpha;
+                acc[j] *= alpha;
+#pragma unroll
+                for (int k = 0; k < kChunkBatch; k++) {
+                    if (lv[j][k] == -INFINITY) continue;  // empty chunk: no weight
+                    const float w = expf(lv[j][k] - mb);
+                    s[j] += w;
+                    acc[j] += w * ov[j][k];
+                }
+                m[j] = mb;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kUnits; j++) {
+            if (!ok[j]) continue;
+            const int u = u0 + j * nthr;
+            const int hq = hq0 + u / q4, d0 = (u % q4) * 4;
+            const int64_t row = (int64_t)b * Hq + hq;
+            merge_bf16x4 ob;
+            if (m[j] == -INFINITY) {
+                ob = merge_bf16x4{};
+                if (d0 == 0) lse[row] = -INFINITY;
+            } else {
+                const float inv = 1.0f / s[j];
+#pragma unroll
+                for (int k = 0; k < 4; k++) ob[k] = (__bf16)(acc[j][k] * inv);
+                if (d0 == 0) lse[row] = m[j] + logf(s[j]);
+            }
+            *(merge_bf16x4 *)(out + row * Dv + d0) = ob;
+        }
+    }
+}
+
+// Fused combine, called by every thread of a workgroup once it has processed all its
+// items [ib, ie) (row group rg: query heads [hq0, hq0 + nrows)).  Release: each thread's
+// partial writes are made visible at device scope (one fence per workgroup), then one
+// thread counts each of the workgroup's partial chunks in; the workgroup that counts a
+// request's last chunk acquires the other workgroups' writes, merges that request, and
+// returns its counter to zero.  Then requests with no chunk at all (length 0 under the
+// balanced rule) get out = 0, lse = -inf from workgroup part = b mod num_parts.
+__device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *plan, int part,
+                                          int ib, int ie, int rg, int n_rowgroups, int hq0,
+                                          int nrows, int *s_flag)
+{
+    const int Hq = a.Hkv * a.G;
+    __threadfence();
+    __syncthreads();
+    for (int it = ib; it < ie; it++) {
+        if (plan[a.items_off + 4 * it + 3] & 1) continue;   // single chunk: already final
+        const int b = plan[a.items_off + 4 * it + 0];
+        const int c0 = plan[a.chunk_off_off + b];
+        const int n = plan[a.chunk_off_off + b + 1] - c0;
+        int32_t *cnt = a.counters + (int64_t)b * n_rowgroups + rg;
+        if (threadIdx.x == 0)
+            *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                      n - 1;
+        __syncthreads();
+        if (*s_flag) {
+            __threadfence();
+            merge_rows<4>(a.ws_o, a.ws_lse, a.out, a.lse, b, c0, n, Hq, a.Dv, hq0, nrows,
+                          threadIdx.x, blockDim.x);
+            if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
+    for (int b = part; b < a.B; b += a.num_parts) {
+        if (plan[a.chunk_off_off + b + 1] != plan[a.chunk_off_off + b]) continue;
+        const int q4 = a.Dv / 4;
+        for (int u = threadIdx.x; u < nrows * q4; u += blockDim.x) {
+            const int hq = hq0 + u / q4, d0 = (u % q4) * 4;
+            const int64_t row = (int64_t)b * Hq + hq;
+            *(merge_bf16x4 *)(a.out + row * a.Dv + d0) = merge_bf16x4{};
+            if (d0 == 0) a.lse[row] = -INFINITY;
+        }
+    }
+}
+
+}  // namespace pa

@@ -48,7 +48,8 @@ __device__ int block_exclusive_scan(int *v, int n, int *scratch)
 
 __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
     const int32_t *__restrict__ seq_lens, int32_t *__restrict__ plan, int B, int num_parts,
-    int max_items, int num_splits, int part_begin_off, int chunk_off_off, int items_off)
+    int max_items, int num_splits, int part_begin_off, int chunk_off_off, int items_off,
+    int counters_off, int n_counters)
 {
     __shared__ int s_start[kMaxBatch + 1];   // tile prefix S_b
     __shared__ int s_ne[kMaxBatch + 1];      // non-empty request prefix
@@ -57,6 +58,8 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
     int32_t *part_begin = plan + part_begin_off;
     int32_t *chunk_off = plan + chunk_off_off;
     int32_t *items = plan + items_off;
+    // fused-combine counters start at zero (each fused run leaves them at zero again)
+    for (int i = tid; i < n_counters; i += kPlanThreads) plan[counters_off + i] = 0;
 
     if (num_splits > 0) {
         // ---- fixed split count: item p = (b = p / s, i = p % s), one per part
@@ -220,7 +223,7 @@ hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout 
 {
     hipLaunchKernelGGL(pa_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, plan,
                        L.B, L.num_parts, L.max_items, num_splits, L.part_begin_off,
-                       L.chunk_off_off, L.items_off);
+                       L.chunk_off_off, L.items_off, L.counters_off, L.n_counters);
     return hipGetLastError();
 }
 

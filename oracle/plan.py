@@ -22,6 +22,7 @@ Plan buffer (int32 words), shared contract with the library:
   [0] magic 0x50414450  [1] mode (0 fixed, 1 balanced)  [2] B  [3] num_parts
   [4] num_items  [5] T  [6] max_items  [7] 0
   part_begin[num_parts + 1] | chunk_off[B + 1] | items[max_items][4] = (b, tok0, tok1, flags)
+  | counters[B * n_rowgroups] (all zero: finished-chunk counters of the fused combine)
   flags bit 0: the request has exactly one chunk (its item writes the final output).
 """
 from __future__ import annotations
@@ -78,11 +79,13 @@ def max_items(B: int, num_splits: int, num_parts: int) -> int:
     return B * num_splits if num_splits > 0 else num_parts + B
 
 
-def plan_words(seq_lens, num_splits: int, num_parts: int, tile: int = TILE) -> np.ndarray:
+def plan_words(seq_lens, num_splits: int, num_parts: int, tile: int = TILE,
+               n_rowgroups: int = 0) -> np.ndarray:
     """The full plan buffer (int32) the plan kernel must write, for either rule.
 
     num_splits > 0 selects the fixed rule (num_parts is then B * num_splits);
     num_splits == 0 selects the balanced rule with ``num_parts`` parts.
+    n_rowgroups: counter words per request appended after the items (zero).
     """
     B = len(seq_lens)
     if num_splits > 0:
@@ -104,7 +107,7 @@ def plan_words(seq_lens, num_splits: int, num_parts: int, tile: int = TILE) -> n
     for (_p, b, _t0, _t1) in flat:
         per_req[b] += 1
     chunk_off = np.concatenate([[0], np.cumsum(per_req)])
-    words = np.zeros(HEADER_WORDS + (P + 1) + (B + 1) + 4 * mi, np.int64)
+    words = np.zeros(HEADER_WORDS + (P + 1) + (B + 1) + 4 * mi + B * n_rowgroups, np.int64)
     words[0:8] = [MAGIC, mode, B, P, nitems, tile, mi, 0]
     o = HEADER_WORDS
     words[o:o + P + 1] = part_begin
@@ -121,6 +124,13 @@ def valid_words(words: np.ndarray) -> int:
     """Number of leading words that are defined (header + arrays + used items)."""
     P, B, nitems = int(words[3]), int(words[2]), int(words[4])
     return HEADER_WORDS + (P + 1) + (B + 1) + 4 * nitems
+
+
+def counters_slice(words: np.ndarray, n_rowgroups: int) -> slice:
+    """Position of the fused-combine counter words in a plan buffer."""
+    P, B, mi = int(words[3]), int(words[2]), int(words[6])
+    o = HEADER_WORDS + (P + 1) + (B + 1) + 4 * mi
+    return slice(o, o + B * n_rowgroups)
 
 
 def items_of(words: np.ndarray):

@@ -36,9 +36,9 @@ def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
 class GpuRun:
     """Plan + decode + combine for one instance and split setting."""
 
-    def __init__(self, case: dict, num_splits=None, dev=None, poison=True):
+    def __init__(self, case: dict, num_splits=None, dev=None, poison=True, fused=False):
         self.case = case
-        self.desc = pb.desc_from_case(case, num_splits)
+        self.desc = pb.desc_from_case(case, num_splits, fused=fused)
         self.dev = dev if dev is not None else to_device(case)
         B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
         self.runner = pb.PagedDecode(self.desc)

@@ -52,6 +52,8 @@ BAD = [
     (dict(s_tok=4), pb.PA_ERR_INVALID),          # 8-byte stride: not 16-byte aligned
     (dict(s_tok=56), pb.PA_ERR_INVALID),         # not a multiple of 16 bytes... 112 B
     (dict(num_splits=-1), pb.PA_ERR_INVALID),
+    (dict(flags=2), pb.PA_ERR_INVALID),           # undefined flag bit
+    (dict(flags=-1), pb.PA_ERR_INVALID),
     (dict(kv_format=7), pb.PA_ERR_INVALID),
     (dict(D=96, Dv=96, s_tok=96, s_head=16 * 96, s_page=16 * 96), pb.PA_ERR_UNSUPPORTED),
     (dict(D=128, Dv=64), pb.PA_ERR_UNSUPPORTED),
@@ -62,6 +64,8 @@ BAD = [
     (dict(B=5000), pb.PA_ERR_UNSUPPORTED),
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
      pb.PA_ERR_UNSUPPORTED),
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
+          flags=1), pb.PA_ERR_UNSUPPORTED),      # MLA chunks merge in the combine kernel
 ]
 
 
@@ -76,9 +80,22 @@ def test_size_query_fixed_splits_needs_no_device():
     st, pbytes, wbytes = _plan_status(_desc(num_splits=2))
     assert st == pb.PA_OK
     B, s = 2, 2
-    assert pbytes == 4 * (8 + (B * s + 1) + (B + 1) + 4 * B * s)
+    # header | part_begin | chunk_off | items | fused-combine counters (B x Hkv)
+    assert pbytes == 4 * (8 + (B * s + 1) + (B + 1) + 4 * B * s + B * 1)
     o = (B * s * 1 * 8 * 64 * 4 + 255) // 256 * 256
     assert wbytes == o + B * s * 1 * 8 * 4
+
+
+def test_fused_flag_accepted_and_combine_is_launch_free():
+    st, pbytes, _ = _plan_status(_desc(num_splits=2, flags=pb.PA_FLAG_FUSED_COMBINE))
+    assert st == pb.PA_OK and pbytes > 0
+    # with the flag, combine returns before touching the device (no stream, no launch)
+    d = _desc(num_splits=2, flags=pb.PA_FLAG_FUSED_COMBINE)
+    buf = ctypes.create_string_buffer(1 << 12)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    p = ctypes.c_void_p
+    assert pb.lib().pa_decode_combine(ctypes.byref(d), p(base), p(base), p(base), p(base),
+                                      None) == pb.PA_OK
 
 
 def test_run_rejects_null_and_misaligned_pointers():

@@ -54,7 +54,7 @@ def test_plan_words_match_oracle(lens, splits):
     desc = pb.make_desc(B, 8, 4, 128, 128, 16, 1 << 20, 1 << 14, 8 * 16 * 128, 16 * 128, 128,
                         splits, pb.PA_KV_BF16)
     np_ = pb.pa_decode_num_parts(desc)
-    ref = oplan.plan_words(list(lens), splits, np_)
+    ref = oplan.plan_words(list(lens), splits, np_, n_rowgroups=8)
     pbytes, _ = pb.pa_decode_plan(desc)
     assert pbytes == ref.size * 4
     plan_t = torch.full(((pbytes + 3) // 4,), -7, dtype=torch.int32, device="cuda")
@@ -64,6 +64,8 @@ def test_plan_words_match_oracle(lens, splits):
     got = plan_t.cpu().numpy()
     n = oplan.valid_words(ref)
     assert np.array_equal(got[:n], ref[:n])
+    cs = oplan.counters_slice(ref, 8)
+    assert np.array_equal(got[cs], ref[cs])           # counters zeroed
 
 
 # ---------------------------------------------------------------------------- small parity
