@@ -65,6 +65,7 @@ class CaseSpec:
     loguniform: Optional[tuple] = None   # (lo, hi): draw seq_lens log-uniformly
     num_splits: int = 0
     name: str = ""
+    q_len: int = 1                       # query tokens per request (draft length)
     extra: dict = field(default_factory=dict)
 
 
@@ -99,7 +100,8 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
 
     Keys: B, Hkv, G, D, Dv, page_size, num_pages, max_pages, s_page, s_head, s_tok
     (pool strides in storage units: bf16 elements, or bytes for fp8 / MLA),
-    kv_format, layout, q [B,Hq,D] uint16 (bf16 bits), k_pool, v_pool (None for MLA),
+    kv_format, layout, q [B,Hq,D] uint16 (bf16 bits; [B,q_len,Hq,D] when q_len > 1),
+    q_len, k_pool, v_pool (None for MLA),
     k_scale, v_scale ([num_pages, Hkv] float32 or None), block_table [B, max_pages]
     int32, seq_lens [B] int32, scale (float), num_splits.
     """
@@ -125,9 +127,10 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
         block_table[b, :n] = perm[pos:pos + n]
         pos += n
 
-    q = f32_to_bf16_bits(_normal_f32(rng, (B, Hq, D)))
+    nq = spec.q_len
+    q = f32_to_bf16_bits(_normal_f32(rng, (B, Hq, D) if nq == 1 else (B, nq, Hq, D)))
 
-    case = dict(B=B, Hkv=Hkv, G=G, D=D, Dv=Dv, page_size=P, num_pages=num_pages,
+    case = dict(B=B, Hkv=Hkv, G=G, D=D, Dv=Dv, page_size=P, num_pages=num_pages, q_len=nq,
                 max_pages=max_pages, kv_format=spec.kv_format, layout=spec.layout,
                 q=q, block_table=block_table, seq_lens=seq_lens.astype(np.int32),
                 scale=float(scale if scale is not None else 1.0 / math.sqrt(D)),

@@ -33,7 +33,7 @@ class _Desc(ctypes.Structure):
         ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("max_pages", ctypes.c_int32),
         ("s_page", ctypes.c_int64), ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64),
-        ("kv_format", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("q_len", ctypes.c_int32),
     ]
 
 
@@ -61,7 +61,7 @@ def lib():
         L.oracle_decode.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_double, vp, vp, vp, ctypes.c_int]
         L.oracle_decode.restype = ctypes.c_int
-        L.oracle_ranges.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp,
+        L.oracle_ranges.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_double, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_int]
         L.oracle_ranges.restype = ctypes.c_int
@@ -92,7 +92,7 @@ def _c(a, dtype=None):
 def _desc(case) -> _Desc:
     return _Desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
                  case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
-                 case["s_tok"], case["kv_format"])
+                 case["s_tok"], case["kv_format"], case.get("q_len", 1))
 
 
 def _arrays(case):
@@ -110,18 +110,27 @@ def threads(n: int = 0) -> int:
     return lib().oracle_threads(n)
 
 
+def _rows_shape(case):
+    """Leading output shape: (B, Hq) for one query token, (B, q_len, Hq) for several."""
+    nq = case.get("q_len", 1)
+    Hq = case["Hkv"] * case["G"]
+    return (case["B"], Hq) if nq == 1 else (case["B"], nq, Hq)
+
+
 def decode(case, scale=None, pairs=None, nthreads: int = 0):
     """Plain definition for every (b, h) pair (or the boolean mask ``pairs`` [B, Hkv]).
 
-    Returns (out [B, Hq, Dv] float64, lse [B, Hq] float64); rows of skipped pairs are NaN.
+    Returns (out [B, Hq, Dv] float64, lse [B, Hq] float64) - with q_len > 1 query
+    tokens per request, out [B, q_len, Hq, Dv] and lse [B, q_len, Hq]; rows of skipped
+    pairs are NaN.
     """
     B, Hkv, G, Dv = case["B"], case["Hkv"], case["G"], case["Dv"]
     q, k, v, ks, vs, bt = _arrays(case)
     sl = _c(case["seq_lens"], np.int32)
     sc = float(case["scale"] if scale is None else scale)
     mask = None if pairs is None else _c(np.asarray(pairs, dtype=bool).reshape(B, Hkv), np.uint8)
-    out = np.full((B, Hkv * G, Dv), np.nan)
-    lse = np.full((B, Hkv * G), np.nan)
+    out = np.full(_rows_shape(case) + (Dv,), np.nan)
+    lse = np.full(_rows_shape(case), np.nan)
     d = _desc(case)
     rc = lib().oracle_decode(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
                              _ptr(bt), _ptr(sl), sc, _ptr(mask), _ptr(out), _ptr(lse), nthreads)
@@ -134,20 +143,24 @@ def ranges(case, rb, rt0, rt1, scale=None, nthreads: int = 0):
     """Partial triples (m, l, Ot) of the XQA multi-block merge for token ranges.
 
     rb, rt0, rt1: request index and [begin, end) token range of each range.
-    Returns m, l [n, Hkv, G] and Ot [n, Hkv, G, Dv] (unnormalised), float64.
+    Returns m, l [n, Hkv, G] and Ot [n, Hkv, G, Dv] (unnormalised), float64; with
+    q_len > 1 query tokens, [n, q_len, Hkv, G] and [n, q_len, Hkv, G, Dv].
     """
     Hkv, G, Dv = case["Hkv"], case["G"], case["Dv"]
+    nq = case.get("q_len", 1)
     q, k, v, ks, vs, bt = _arrays(case)
+    sl = _c(case["seq_lens"], np.int32)
     rb, rt0, rt1 = _c(rb, np.int32), _c(rt0, np.int32), _c(rt1, np.int32)
     n = int(rb.shape[0])
-    m = np.zeros((n, Hkv, G))
-    l = np.zeros((n, Hkv, G))
-    Ot = np.zeros((n, Hkv, G, Dv))
+    lead = (n, Hkv, G) if nq == 1 else (n, nq, Hkv, G)
+    m = np.zeros(lead)
+    l = np.zeros(lead)
+    Ot = np.zeros(lead + (Dv,))
     sc = float(case["scale"] if scale is None else scale)
     d = _desc(case)
     rc = lib().oracle_ranges(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
-                             _ptr(bt), sc, n, _ptr(rb), _ptr(rt0), _ptr(rt1), _ptr(m), _ptr(l),
-                             _ptr(Ot), nthreads)
+                             _ptr(bt), _ptr(sl), sc, n, _ptr(rb), _ptr(rt0), _ptr(rt1), _ptr(m),
+                             _ptr(l), _ptr(Ot), nthreads)
     if rc != 0:
         raise MemoryError("oracle_ranges failed")
     return m, l, Ot
@@ -175,22 +188,23 @@ def split_decode(case, items, scale=None, nthreads: int = 0):
     """Split-KV evaluation: partial triples per (request, token range) item, merged per
     request with the XQA formula.  ``items`` is a list of (b, t0, t1).
 
-    Returns (out [B, Hq, Dv], lse [B, Hq]) and the per-item partials (m, l, Ot).
+    Returns (out, lse) shaped like ``decode``'s and the per-item partials (m, l, Ot).
     """
-    B, Hkv, G, Dv = case["B"], case["Hkv"], case["G"], case["Dv"]
+    B, Dv = case["B"], case["Dv"]
     rb = np.array([it[0] for it in items], np.int32)
     rt0 = np.array([it[1] for it in items], np.int32)
     rt1 = np.array([it[2] for it in items], np.int32)
     m, l, Ot = ranges(case, rb, rt0, rt1, scale=scale, nthreads=nthreads)
-    out = np.zeros((B, Hkv * G, Dv))
-    lse = np.full((B, Hkv * G), -np.inf)
+    rows = _rows_shape(case)[1:]
+    out = np.zeros((B,) + rows + (Dv,))
+    lse = np.full((B,) + rows, -np.inf)
     for b in range(B):
         sel = np.nonzero(rb == b)[0]
         if sel.size == 0:
             continue
         O, ls = merge(m[sel], l[sel], Ot[sel])
-        out[b] = O.reshape(Hkv * G, Dv)
-        lse[b] = ls.reshape(Hkv * G)
+        out[b] = O.reshape(rows + (Dv,))
+        lse[b] = ls.reshape(rows)
     return out, lse, (m, l, Ot)
 
 

@@ -21,6 +21,14 @@
  * log-sum-exp of the scaled logits is used).  An empty token range gives out = 0
  * and lse = -inf.
  *
+ * Several query tokens per request (speculative decoding with a linear draft; XQA
+ * article, section "投机解码: XQA 的第二个工作负载"): the q_len draft tokens are the
+ * last q_len positions of the request, their K/V already in the cache (the KV append
+ * happens before attention, same article, section "一次 decode step 的完整时序"), and
+ * a chain draft lets draft token i see the cached context and the draft tokens up to
+ * itself: query token i (0-based) attends to tokens [0, L - q_len + i + 1).  q is
+ * [B][q_len][Hq][D], out [B][q_len][Hq][Dv], lse [B][q_len][Hq].
+ *
  * Pins: see tests/test_oracle.py (dense library attention, closed forms,
  * invariances, the rescale worked example, all 256 e4m3 codes).
  */
@@ -157,7 +165,7 @@ static void fetch(const oracle_desc *d, const void *k_pool, const void *v_pool,
  */
 static int range_state(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                        const void *v_pool, const float *k_scale, const float *v_scale,
-                       const int32_t *block_table, double scale, int b, int h, int t0,
+                       const int32_t *block_table, double scale, int b, int h, int qi, int t0,
                        int t1, double *m, double *l, double *Ot)
 {
     const int G = d->G, D = d->D, Dv = d->Dv;
@@ -183,7 +191,8 @@ static int range_state(const oracle_desc *d, const uint16_t *q, const void *k_po
     const int Hq = d->Hkv * G;
     for (int g = 0; g < G; g++)
         for (int i = 0; i < D; i++)
-            qf[(int64_t)g * D + i] = oracle_bf16_to_f64(q[((int64_t)b * Hq + (int64_t)h * G + g) * D + i]);
+            qf[(int64_t)g * D + i] = oracle_bf16_to_f64(
+                q[(((int64_t)b * d->q_len + qi) * Hq + (int64_t)h * G + g) * D + i]);
 
     /* pass 1: logits */
     for (int t = t0; t < t1; t++) {
@@ -232,34 +241,43 @@ static int set_threads(int nthreads)
 
 int oracle_threads(int nthreads) { return set_threads(nthreads); }
 
+/* Causal limit of query token qi of a request of length L: it sees tokens [0, lim). */
+static int causal_limit(const oracle_desc *d, int L, int qi)
+{
+    const int lim = L - (d->q_len - 1 - qi);
+    return lim > 0 ? lim : 0;
+}
+
 /*
  * Whole-request attention for every (b, h) with pair_mask[b*Hkv+h] != 0
- * (pair_mask NULL: all pairs):  out = Ot / l,  lse = m + ln l.
- * out is [B][Hq][Dv], lse is [B][Hq]; rows of skipped pairs are left untouched.
+ * (pair_mask NULL: all pairs):  out = Ot / l,  lse = m + ln l, for each query token.
+ * out is [B][q_len][Hq][Dv], lse is [B][q_len][Hq]; rows of skipped pairs are left
+ * untouched.
  */
 int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
                   const int32_t *block_table, const int32_t *seq_lens, double scale,
                   const uint8_t *pair_mask, double *out, double *lse, int nthreads)
 {
-    const int B = d->B, Hkv = d->Hkv, G = d->G, Dv = d->Dv, Hq = Hkv * G;
+    const int B = d->B, Hkv = d->Hkv, G = d->G, Dv = d->Dv, Hq = Hkv * G, nq = d->q_len;
     int err = 0;
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
-    for (int64_t pr = 0; pr < (int64_t)B * Hkv; pr++) {
-        const int b = (int)(pr / Hkv), h = (int)(pr % Hkv);
-        if (pair_mask && !pair_mask[pr])
+    for (int64_t pr = 0; pr < (int64_t)B * Hkv * nq; pr++) {
+        const int b = (int)(pr / ((int64_t)Hkv * nq));
+        const int h = (int)((pr / nq) % Hkv), qi = (int)(pr % nq);
+        if (pair_mask && !pair_mask[(int64_t)b * Hkv + h])
             continue;
         double *m = (double *)malloc(sizeof(double) * (size_t)G);
         double *l = (double *)malloc(sizeof(double) * (size_t)G);
         double *Ot = (double *)malloc(sizeof(double) * (size_t)G * Dv);
         if (!m || !l || !Ot ||
-            range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h, 0,
-                        seq_lens[b], m, l, Ot) != 0) {
+            range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h, qi, 0,
+                        causal_limit(d, seq_lens[b], qi), m, l, Ot) != 0) {
             err |= 1;
         } else {
             for (int g = 0; g < G; g++) {
-                const int64_t row = (int64_t)b * Hq + (int64_t)h * G + g;
+                const int64_t row = ((int64_t)b * nq + qi) * Hq + (int64_t)h * G + g;
                 if (l[g] > 0.0) {
                     for (int i = 0; i < Dv; i++)
                         out[row * Dv + i] = Ot[(int64_t)g * Dv + i] / l[g];
@@ -280,23 +298,33 @@ int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
 
 /*
  * Partial triples for a list of n token ranges (request rb[i], tokens
- * [rt0[i], rt1[i])), for every KV head:
- *   m, l : [n][Hkv][G]     Ot : [n][Hkv][G][Dv]
+ * [rt0[i], rt1[i])), for every query token and KV head; query token qi only sees the
+ * part of the range below its causal limit (seq_lens may be NULL when q_len == 1):
+ *   m, l : [n][q_len][Hkv][G]     Ot : [n][q_len][Hkv][G][Dv]
  */
 int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, double scale, int n, const int32_t *rb,
-                  const int32_t *rt0, const int32_t *rt1, double *m, double *l, double *Ot,
-                  int nthreads)
+                  const int32_t *block_table, const int32_t *seq_lens, double scale, int n,
+                  const int32_t *rb, const int32_t *rt0, const int32_t *rt1, double *m,
+                  double *l, double *Ot, int nthreads)
 {
-    const int Hkv = d->Hkv, G = d->G, Dv = d->Dv;
+    const int Hkv = d->Hkv, G = d->G, Dv = d->Dv, nq = d->q_len;
+    if (nq > 1 && !seq_lens)
+        return -1;
     int err = 0;
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
-    for (int64_t pr = 0; pr < (int64_t)n * Hkv; pr++) {
-        const int i = (int)(pr / Hkv), h = (int)(pr % Hkv);
-        if (range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, rb[i], h,
-                        rt0[i], rt1[i], m + pr * G, l + pr * G, Ot + pr * (int64_t)G * Dv) != 0)
+    for (int64_t pr = 0; pr < (int64_t)n * nq * Hkv; pr++) {
+        const int i = (int)(pr / ((int64_t)nq * Hkv));
+        const int qi = (int)((pr / Hkv) % nq), h = (int)(pr % Hkv);
+        int t1 = rt1[i];
+        if (nq > 1) {
+            const int lim = causal_limit(d, seq_lens[rb[i]], qi);
+            if (t1 > lim)
+                t1 = lim;
+        }
+        if (range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, rb[i], h, qi,
+                        rt0[i], t1, m + pr * G, l + pr * G, Ot + pr * (int64_t)G * Dv) != 0)
             err |= 1;
     }
     return err ? -1 : 0;

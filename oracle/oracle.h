@@ -19,6 +19,7 @@ typedef struct {
        bytes for ORACLE_KV_FP8_PAGE_HEAD and ORACLE_KV_MLA656 */
     int64_t s_page, s_head, s_tok;
     int32_t kv_format;
+    int32_t q_len;   /* query tokens per request (1: plain decode) */
 } oracle_desc;
 
 double oracle_bf16_to_f64(uint16_t bits);
@@ -34,7 +35,8 @@ int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
 
 int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, double scale, int n, const int32_t *rb,
+                  const int32_t *block_table, const int32_t *seq_lens, double scale, int n,
+                  const int32_t *rb,
                   const int32_t *rt0, const int32_t *rt1, double *m, double *l, double *Ot,
                   int nthreads);
 

@@ -333,3 +333,96 @@ def test_merge_skips_empty_partials():
     assert abs(lse[0] - (1.0 + math.log(2.0))) < 1e-15
     O, lse = oracle.merge(np.array([[-np.inf], [-np.inf]]), np.zeros((2, 1)), np.zeros((2, 1, 3)))
     assert np.all(O == 0) and np.isneginf(lse[0])
+
+
+# --------------------------------------------------------------------------------------
+# Several query tokens per request (linear draft, causal within the draft)
+# --------------------------------------------------------------------------------------
+
+def spec_case(q_len, fmt=synth.KV_BF16, B=3, Hq=8, Hkv=2, D=64, P=16, lens=(37, 64, 129),
+              seed=9):
+    used = sum(-(-L // P) for L in lens)
+    spec = synth.CaseSpec(B=B, Hq=Hq, Hkv=Hkv, D=D, Dv=D, page_size=P, seq_lens=lens,
+                          kv_format=fmt, pool_pages=used + 3, q_len=q_len)
+    return synth.make_case(spec, seed)
+
+
+def library_attention_multi(case):
+    """Library path with an explicit boolean mask: query token i of a request of length L
+    may see key t iff t <= L - q_len + i.  torch SDPA (float64) + scipy logsumexp."""
+    B, Hkv, G, Dv, nq = case["B"], case["Hkv"], case["G"], case["Dv"], case["q_len"]
+    sc = case["scale"]
+    q = _bf16_to_f64(case["q"])                                 # [B, nq, Hq, D]
+    out = np.zeros((B, nq, Hkv * G, Dv))
+    lse = np.full((B, nq, Hkv * G), -np.inf)
+    for b in range(B):
+        L = int(case["seq_lens"][b])
+        allowed = np.arange(L)[None, :] <= (L - nq + np.arange(nq))[:, None]     # [nq, L]
+        for h in range(Hkv):
+            K, V = dense_kv(case, b, h)
+            for g in range(G):
+                hq = h * G + g
+                qq = q[b, :, hq]                                # [nq, D]
+                rows = allowed.any(axis=1)
+                o = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(qq[rows])[None], torch.from_numpy(K)[None],
+                    torch.from_numpy(V)[None], attn_mask=torch.from_numpy(allowed[rows])[None],
+                    scale=sc)
+                out[b, rows, hq] = o[0].numpy()
+                logits = np.where(allowed, sc * (qq @ K.T), -np.inf)
+                lse[b, rows, hq] = scipy.special.logsumexp(logits[rows], axis=1)
+    return out, lse
+
+
+@pytest.mark.parametrize("q_len,kw", [(2, {}), (4, dict(Hq=16, Hkv=4, D=128, P=32)),
+                                      (3, dict(fmt=synth.KV_FP8_PAGE_HEAD, D=128)),
+                                      (5, dict(lens=(5, 6, 40))), (2, dict(lens=(1, 2, 17)))])
+def test_multi_token_matches_library_masked_attention(q_len, kw):
+    case = spec_case(q_len, **kw)
+    out, lse = oracle.decode(case)
+    ref_out, ref_lse = library_attention_multi(case)
+    assert out.shape == ref_out.shape
+    np.testing.assert_allclose(out, ref_out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_multi_token_first_draft_token_of_a_draft_only_request():
+    """L = q_len: draft token 0 sees only key 0, so its output is v_0 and its lse s_0;
+    a request shorter than the draft leaves its first tokens with nothing to see."""
+    case = spec_case(3, lens=(3, 2, 20))
+    out, lse = oracle.decode(case)
+    G = case["G"]
+    q = _bf16_to_f64(case["q"])
+    for h in range(case["Hkv"]):
+        K, V = dense_kv(case, 0, h)
+        for g in range(G):
+            np.testing.assert_allclose(out[0, 0, h * G + g], V[0], rtol=0, atol=1e-15)
+            s0 = case["scale"] * float(q[0, 0, h * G + g] @ K[0])
+            assert abs(lse[0, 0, h * G + g] - s0) < 1e-13
+    assert np.all(out[1, 0] == 0) and np.all(np.isneginf(lse[1, 0]))
+    assert np.all(np.isfinite(lse[1, 1:]))
+
+
+def test_multi_token_last_draft_token_is_plain_decode():
+    """The last draft token sees the whole request: it equals one-token decode of that q."""
+    case = spec_case(4, Hq=8, Hkv=2, D=128, P=16, lens=(100, 33, 7))
+    out, lse = oracle.decode(case)
+    one = dict(case, q=np.ascontiguousarray(case["q"][:, -1]), q_len=1)
+    out1, lse1 = oracle.decode(one)
+    np.testing.assert_array_equal(out[:, -1], out1)
+    np.testing.assert_array_equal(lse[:, -1], lse1)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_multi_token_split_merge_equals_whole(splits):
+    from oracle import plan
+    case = spec_case(3, lens=(3, 130, 257))
+    items = plan.fixed_items(case["seq_lens"], splits)
+    out1, lse1, _ = oracle.split_decode(case, items)
+    out0, lse0 = oracle.decode(case)
+    np.testing.assert_allclose(out1, out0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(lse1), np.isneginf(lse0))
+    fin = np.isfinite(lse0)
+    np.testing.assert_allclose(lse1[fin], lse0[fin], rtol=1e-13, atol=1e-12)
