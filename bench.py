@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload index (default 1)")
     ap.add_argument("--batch", type=int, default=None, help="batch of the HD64 workload (1 or 8)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per request (linear speculative draft)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
@@ -77,7 +79,8 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.time()
-    case = synth.config_case(args.config, B=args.batch)
+    case = synth.config_case(args.config, B=args.batch, **({"q_len": args.q_len}
+                                                           if args.q_len != 1 else {}))
     gen_s = time.time() - t_gen
     print(f"[bench] generated workload {args.config} ({case['name']}) in {gen_s:.1f}s", file=sys.stderr,
           flush=True)
@@ -94,8 +97,8 @@ def main():
     vs = dev(case["v_scale"]) if case.get("v_scale") is not None else None
     bt, sl = dev(case["block_table"]), dev(case["seq_lens"])
     B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
-    out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, args.q_len, Hq, Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, args.q_len, Hq), dtype=torch.float32, device="cuda")
     desc = pb.desc_from_case(case, fused=args.fused_combine)
     runner = pb.PagedDecode(desc)
     stream = torch.cuda.current_stream()
@@ -196,7 +199,7 @@ def main():
 
     cfg = {"workload": case["name"], "B": B, "Hq": Hq, "Hkv": case["Hkv"], "D": case["D"],
            "Dv": Dv, "page_size": case["page_size"], "seq_len_total": int(np.sum(case["seq_lens"])),
-           "kv_format": fmt, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
+           "kv_format": fmt, "q_len": args.q_len, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
            "num_parts": pb.pa_decode_num_parts(desc),
            "combine": "fused in the decode kernel" if args.fused_combine else "combine kernel",
            "parallelism": "single GPU"}

@@ -74,13 +74,13 @@ def make_desc(B, Hkv, G, D, Dv, page_size, num_pages, max_pages_per_seq, s_page,
                         s_head, s_tok, q_len, num_splits, kv_format, flags)
 
 
-def desc_from_case(case: dict, num_splits: Optional[int] = None, fused: bool = False,
-                   q_len: int = 1) -> PaDecodeDesc:
+def desc_from_case(case: dict, num_splits: Optional[int] = None,
+                   fused: bool = False) -> PaDecodeDesc:
     """Descriptor for an instance drawn by ``mqa_split_kv_amd.synth``."""
     ns = case["num_splits"] if num_splits is None else num_splits
     return make_desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
                      case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
-                     case["s_tok"], ns, case["kv_format"], q_len=q_len,
+                     case["s_tok"], ns, case["kv_format"], q_len=case.get("q_len", 1),
                      flags=PA_FLAG_FUSED_COMBINE if fused else 0)
 
 

@@ -12,6 +12,7 @@ namespace {
 using pa::PlanLayout;
 
 constexpr int kMaxDevices = 64;
+constexpr int kMaxQLen = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device (queried once per device).
@@ -50,7 +51,7 @@ pa_status check_desc(const pa_decode_desc *d)
     const int64_t eb = elem_bytes(d->kv_format);
     if ((d->s_page * eb) % 16 || (d->s_head * eb) % 16 || (d->s_tok * eb) % 16) return PA_ERR_INVALID;
     if ((int64_t)d->Hkv * d->G > 65536) return PA_ERR_UNSUPPORTED;
-    if (d->q_len != 1) return PA_ERR_UNSUPPORTED;
+    if (d->q_len > kMaxQLen) return PA_ERR_UNSUPPORTED;
     const int P = d->page_size;
     if (P != 16 && P != 32 && P != 64 && P != 128 && P != 256) return PA_ERR_UNSUPPORTED;
     if (d->B > pa::kMaxBatch) return PA_ERR_UNSUPPORTED;
@@ -60,6 +61,7 @@ pa_status check_desc(const pa_decode_desc *d)
         // the MLA kernel keeps its whole register file for the tile loop; its chunks are
         // merged by the combine kernel only
         if (d->flags & PA_FLAG_FUSED_COMBINE) return PA_ERR_UNSUPPORTED;
+        if (d->q_len != 1) return PA_ERR_UNSUPPORTED;
         if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
         if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
         if (d->s_tok < 656) return PA_ERR_INVALID;
@@ -67,6 +69,7 @@ pa_status check_desc(const pa_decode_desc *d)
     }
     if (d->D != d->Dv || (d->D != 64 && d->D != 128)) return PA_ERR_UNSUPPORTED;
     if (d->G > 16) return PA_ERR_UNSUPPORTED;
+    if (d->G * d->q_len > 256) return PA_ERR_UNSUPPORTED;   // 16 column tiles of 16 rows
     // a token row must fit inside the stride it is read with
     if (d->s_tok < d->D) return PA_ERR_INVALID;
     return PA_OK;
@@ -143,7 +146,8 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
     st = layout_for(desc, &L);
     if (st != PA_OK) return st;
     const size_t pbytes = L.words * 4;
-    const size_t wbytes = pa::ws_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv);
+    const size_t wbytes =
+        pa::ws_bytes(L.max_items, desc->q_len * desc->Hkv * desc->G, desc->Dv);
     if (!plan) {
         if (plan_bytes) *plan_bytes = pbytes;
         if (workspace_bytes) *workspace_bytes = wbytes;
@@ -197,8 +201,11 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
     a.lse = lse;
     a.ws_o = (float *)workspace;
     a.ws_lse = workspace ? (float *)((uint8_t *)workspace +
-                                     pa::ws_o_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv))
+                                     pa::ws_o_bytes(L.max_items,
+                                                    desc->q_len * desc->Hkv * desc->G, desc->Dv))
                          : nullptr;
+    a.seq_lens = seq_lens;
+    a.q_len = desc->q_len;
     a.s_page_b = desc->s_page * eb;
     a.s_head_b = desc->s_head * eb;
     a.s_tok_b = desc->s_tok * eb;
@@ -240,9 +247,11 @@ pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const 
     if (st != PA_OK) return st;
     const float *ws_o = (const float *)workspace;
     const float *ws_lse = (const float *)((const uint8_t *)workspace +
-                                          pa::ws_o_bytes(L.max_items, desc->Hkv, desc->G, desc->Dv));
+                                          pa::ws_o_bytes(L.max_items,
+                                                         desc->q_len * desc->Hkv * desc->G,
+                                                         desc->Dv));
     if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, (uint16_t *)out, lse, desc->B,
-                           desc->Hkv, desc->G, desc->Dv, L.chunk_off_off,
+                           desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
                            (hipStream_t)stream) != hipSuccess)
         return PA_ERR_DEVICE;
     return PA_OK;

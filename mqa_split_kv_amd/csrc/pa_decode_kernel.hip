@@ -25,6 +25,12 @@
 // FP8 K/V are converted to bf16 exactly in registers; the K scale of a page
 // multiplies that page's logits, the V scale multiplies P before the PV product
 // (XQA article, section "FP8 / INT8 的 KV: 转换到底放在哪儿", scale folding).
+//
+// Several query tokens per request (a linear speculative draft; XQA article, section
+// "投机解码: XQA 的第二个工作负载", which folds draft tokens x GQA heads into the MMA
+// row dimension): the G * q_len query rows of a KV head fill the 16 MFMA columns, more
+// than 16 rows take several column tiles (grid z).  Column (qi, g) masks the keys past
+// its causal limit L - q_len + qi + 1.
 #include "pa_merge.h"
 
 namespace pa {
@@ -166,7 +172,8 @@ __device__ __forceinline__ void load_block(const DecodeArgs &a, const int32_t *_
 template <int D, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void pa_decode_kernel(
     DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt,
-    const float *__restrict__ ksc, const float *__restrict__ vsc)
+    const float *__restrict__ ksc, const float *__restrict__ vsc,
+    const int32_t *__restrict__ seq_lens)
 {
     // read-only tables come in as separate restrict arguments so that their wave-uniform
     // reads compile to scalar loads (a vector load would join the in-order vmcnt queue)
@@ -184,7 +191,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int wave = uniform(threadIdx.x >> 6);
     const int col = lane & 15, g4 = lane >> 4;
     const int part = blockIdx.x, h = blockIdx.y;
-    const int G = a.G, Hq = a.Hkv * a.G;
+    const int G = a.G, Hq = a.Hkv * a.G, nq = a.q_len, rows = G * nq;
+    // this lane's MFMA column: query row c = 16 * blockIdx.z + col = qi * G + g
+    const int c = 16 * blockIdx.z + col;
+    const int cqi = c / G, cg = c - (c / G) * G;
     uint8_t *vt = lds + wave * C::VTILE;
     // lane byte offsets inside a 16-token sub-block: K row `col`, 16-byte chunk g4 (+4u);
     // V chunk `lane` of the row-major chunk order (row lane / CPR, chunk lane % CPR)
@@ -200,18 +210,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int t1 = plan[a.items_off + 4 * it + 2];
         const int flags = plan[a.items_off + 4 * it + 3];
 
-        // ---- Q^T operand (B of the QK MFMA): lane holds head `col`, 8 dims per k-step
+        // ---- Q^T operand (B of the QK MFMA): lane holds query row c, 8 dims per k-step
         bf16x8 qop[C::NS];
         {
-            const uint16_t *qrow = a.q + ((int64_t)b * Hq + (int64_t)h * G + col) * D;
+            const uint16_t *qrow = a.q + (((int64_t)b * nq + cqi) * Hq + (int64_t)h * G + cg) * D;
 #pragma unroll
             for (int s = 0; s < C::NS; s++) {
                 const int d0 = FP8 ? 16 * (4 * (s >> 1) + g4) + 8 * (s & 1) : 8 * (4 * s + g4);
-                if (col < G)
+                if (c < rows)
                     qop[s] = *(const bf16x8 *)(qrow + d0);
                 else
                     qop[s] = bf16x8{};
             }
+        }
+        // keys this column may see in the item: [t0, tlim) (the causal limit of its query
+        // token; every key of the item when q_len = 1)
+        int tlim = t1;
+        if (nq > 1) {
+            const int lim = seq_lens[b] - (nq - 1 - cqi);
+            tlim = lim < t1 ? lim : t1;
         }
 
         float m = -INFINITY;      // running max (log2 domain) of head `col`
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         for (int r = 0; r < 4; r++) {
                             const int tok = tb + 16 * sb + 4 * g4 + r;
                             const float x = st[sb][r] * f;
-                            sv[sb][r] = tok < t1 ? x : -INFINITY;
+                            sv[sb][r] = tok < tlim ? x : -INFINITY;
                             bm = fmaxf(bm, sv[sb][r]);
                         }
                     }
@@ -300,7 +317,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     bm = fmaxf(bm, __shfl_xor(bm, 32));
                     const float mn = fmaxf(m, bm);
                     const float mref = mn == -INFINITY ? 0.f : mn;
-                    const float alpha = fast_exp2(m - mref);
+                    // a column with no visible key yet (its query token's causal limit) keeps
+                    // alpha = 1: its state is still zero
+                    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mref);
                     m = mn;
                     __bf16 pbv[4 * C::NSB];
                     float ps = 0.f;
@@ -308,15 +327,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     for (int sb = 0; sb < C::NSB; sb++) {
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
+                            // the denominator takes the fp32 weight: summing the bf16-rounded
+                            // weights moves lse by up to ~2^-9 when a few keys dominate
                             const float p = fast_exp2(sv[sb][r] - mref);
-                            if (FP8) {
-                                ps += p;
-                                pbv[4 * sb + r] = (__bf16)(p * cur.vs[sb]);
-                            } else {
-                                const __bf16 pr = (__bf16)p;
-                                ps += (float)pr;
-                                pbv[4 * sb + r] = pr;
-                            }
+                            ps += p;
+                            pbv[4 * sb + r] = (__bf16)(FP8 ? p * cur.vs[sb] : p);
                         }
                     }
                     l = l * alpha + ps;
@@ -400,11 +415,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 so[(wave * D + 16 * db + 4 * g4 + r) * 17 + col] = acc[db][r] * f;
         __syncthreads();
 
-        // ---- write: 8 consecutive dims of one head per thread
+        // ---- write: 8 consecutive dims of one query row (column `head`) per thread
         {
             const int t = threadIdx.x;
             const int head = t / (D / 8), d0 = (t % (D / 8)) * 8;
-            if (head < G && t < 16 * (D / 8)) {
+            const int cr = 16 * blockIdx.z + head;
+            if (cr < rows && t < 16 * (D / 8)) {
                 float o[8];
 #pragma unroll
                 for (int k = 0; k < 8; k++) {
@@ -417,7 +433,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 const float lse_v = (Mh == -INFINITY || Lh == 0.f)
                                         ? -INFINITY
                                         : (Mh + log2f(Lh)) * 0.69314718055994530942f;
-                const int64_t row = (int64_t)b * Hq + (int64_t)h * G + head;
+                const int qi = cr / G;
+                const int64_t qr = (int64_t)qi * Hq + (int64_t)h * G + (cr - qi * G);
+                const int64_t row = (int64_t)b * nq * Hq + qr;
                 if (flags & 1) {
                     bf16x8 ob;
 #pragma unroll
@@ -425,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     *(bf16x8 *)(a.out + row * a.Dv + d0) = ob;
                     if (d0 == 0) a.lse[row] = lse_v;
                 } else {
-                    const int64_t prow = ((int64_t)it * a.Hkv + h) * G + head;
+                    const int64_t prow = (int64_t)it * nq * Hq + qr;
                     float *dst = a.ws_o + prow * a.Dv + d0;
                     *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
                     *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
@@ -436,27 +454,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();
     }
     // fused combine: the last workgroup to finish a request's chunks merges them
-    if (a.counters) fused_combine_tail(a, plan, part, ib, ie, h, a.Hkv, h * G, G, &s_flag);
+    if (a.counters)
+        fused_combine_tail(a, plan, part, ib, ie, h, a.Hkv, h * G, G, gridDim.z, &s_flag);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.num_parts, a.Hkv), block(kThreads);
+    const dim3 grid(a.num_parts, a.Hkv, (a.G * a.q_len + 15) / 16), block(kThreads);
     const bool fp8 = a.kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
     if (a.D == 128 && !fp8)
         hipLaunchKernelGGL((pa_decode_kernel<128, false>), grid, block, 0, stream, a, a.plan,
-                           a.block_table, a.k_scale, a.v_scale);
+                           a.block_table, a.k_scale, a.v_scale, a.seq_lens);
     else if (a.D == 64 && !fp8)
         hipLaunchKernelGGL((pa_decode_kernel<64, false>), grid, block, 0, stream, a, a.plan,
-                           a.block_table, a.k_scale, a.v_scale);
+                           a.block_table, a.k_scale, a.v_scale, a.seq_lens);
     else if (a.D == 128 && fp8)
         hipLaunchKernelGGL((pa_decode_kernel<128, true>), grid, block, 0, stream, a, a.plan,
-                           a.block_table, a.k_scale, a.v_scale);
+                           a.block_table, a.k_scale, a.v_scale, a.seq_lens);
     else if (a.D == 64 && fp8)
         hipLaunchKernelGGL((pa_decode_kernel<64, true>), grid, block, 0, stream, a, a.plan,
-                           a.block_table, a.k_scale, a.v_scale);
+                           a.block_table, a.k_scale, a.v_scale, a.seq_lens);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -55,32 +55,36 @@ inline PlanLayout plan_layout(int B, int n_rowgroups, int num_splits, int num_pa
     return L;
 }
 
-// Workspace: normalised fp32 partial outputs [max_items][Hkv][G][Dv], then (256-byte
-// aligned) fp32 partial lse [max_items][Hkv][G] in natural log.
-inline size_t ws_o_bytes(int max_items, int Hkv, int G, int Dv)
+// Workspace: normalised fp32 partial outputs [max_items][q_len][Hkv][G][Dv], then
+// (256-byte aligned) fp32 partial lse [max_items][q_len][Hkv][G] in natural log.  The
+// partial row of query row qr = qi * Hq + hq in chunk c is c * q_len * Hq + qr.
+inline size_t ws_o_bytes(int max_items, int qrows, int Dv)
 {
-    size_t b = (size_t)max_items * Hkv * G * Dv * 4;
+    size_t b = (size_t)max_items * qrows * Dv * 4;
     return (b + 255) & ~(size_t)255;
 }
-inline size_t ws_bytes(int max_items, int Hkv, int G, int Dv)
+inline size_t ws_bytes(int max_items, int qrows, int Dv)
 {
-    return ws_o_bytes(max_items, Hkv, G, Dv) + (size_t)max_items * Hkv * G * 4;
+    return ws_o_bytes(max_items, qrows, Dv) + (size_t)max_items * qrows * 4;
 }
 
 struct DecodeArgs {
-    const uint16_t *q;          // [B][Hq][D] bf16
+    const uint16_t *q;          // [B][q_len][Hq][D] bf16
     const uint8_t *k_pool;      // byte pointers; strides below are in bytes
     const uint8_t *v_pool;
     const float *k_scale;       // [num_pages][Hkv] (fp8 formats)
     const float *v_scale;
     const int32_t *block_table; // [B][max_pages]
     const int32_t *plan;
-    uint16_t *out;              // [B][Hq][Dv] bf16
-    float *lse;                 // [B][Hq]
+    uint16_t *out;              // [B][q_len][Hq][Dv] bf16
+    float *lse;                 // [B][q_len][Hq]
     float *ws_o;
     float *ws_lse;
     int64_t s_page_b, s_head_b, s_tok_b;   // pool strides in bytes
+    const int32_t *seq_lens;    // [B]
     int B, Hkv, G, D, Dv, max_pages, page_shift;
+    int q_len;                  // query tokens per request; query token i sees keys
+                                // [0, L - q_len + i + 1)
     int num_parts, part_begin_off, items_off, chunk_off_off;
     int32_t *counters;          // plan counter words; non-null: fused combine
     float scale_log2;           // logit scale * log2(e)
@@ -92,7 +96,7 @@ hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
-                          uint16_t *out, float *lse, int B, int Hkv, int G, int Dv,
+                          uint16_t *out, float *lse, int B, int Hkv, int G, int q_len, int Dv,
                           int chunk_off_off, hipStream_t stream);
 
 }  // namespace pa

@@ -14,9 +14,11 @@ namespace pa {
 typedef __bf16 merge_bf16x4 __attribute__((ext_vector_type(4)));
 typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 
-// Partial row of query head hq in chunk c: ws_o[(c * Hq + hq) * Dv ...], ws_lse[c * Hq + hq].
-// Merges query heads [hq0, hq0 + nrows) of request b from chunks c0 .. c0 + n - 1.  A work
-// unit is one head and 4 dims; thread tid takes units tid, tid + nthr, ... kUnits at a
+// Query row qr = qi * Hq + hq (query token qi, head hq; nq tokens per request).  Its
+// partial in chunk c is ws_o[(c * nq * Hq + qr) * Dv ...], ws_lse[c * nq * Hq + qr]; its
+// output out[(b * nq * Hq + qr) * Dv ...], lse[b * nq * Hq + qr].  Merges heads
+// [hq0, hq0 + nrows) of every query token of request b from chunks c0 .. c0 + n - 1.  A
+// work unit is one (query token, head) row and 4 dims; thread tid takes units tid, tid + nthr, ... kUnits at a
 // time (1 in the wide combine grid, 4 in a single fused-combine workgroup), and reads the
 // chunks kChunkBatch at a time with a running maximum (the same rescaling as the online
 // softmax), so that up to kUnits x kChunkBatch partial loads are in flight instead of one
@@ -28,11 +30,16 @@ constexpr int kChunkBatch = 4;
 
 template <int kUnits>
 __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16_t *out,
-                                  float *lse, int b, int64_t c0, int n, int Hq, int Dv, int hq0,
-                                  int nrows, int tid, int nthr)
+                                  float *lse, int b, int64_t c0, int n, int Hq, int nq, int Dv,
+                                  int hq0, int nrows, int tid, int nthr)
 {
     const int q4 = Dv / 4;
-    const int total = nrows * q4;
+    const int total = nq * nrows * q4;
+    const int64_t Hr = (int64_t)nq * Hq;                 // query rows per request / chunk
+    auto qrow = [&](int u) {
+        const int rr = u / q4;
+        return (rr / nrows) * Hq + hq0 + rr % nrows;
+    };
     for (int u0 = tid; u0 < total; u0 += kUnits * nthr) {
         int64_t prow0[kUnits];
         bool ok[kUnits];
@@ -42,8 +49,7 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
         for (int j = 0; j < kUnits; j++) {
             const int u = u0 + j * nthr;
             ok[j] = u < total;
-            const int hq = hq0 + (ok[j] ? u / q4 : 0);
-            prow0[j] = c0 * Hq + hq;
+            prow0[j] = c0 * Hr + qrow(ok[j] ? u : 0);
             m[j] = -INFINITY;
             s[j] = 0.f;
             acc[j] = merge_f32x4{0.f, 0.f, 0.f, 0.f};
@@ -57,7 +63,7 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
 #pragma unroll
                 for (int k = 0; k < kChunkBatch; k++) {
                     const bool in = ok[j] && i0 + k < n;
-                    const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hq;
+                    const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hr;
                     lv[j][k] = in ? ws_lse[prow] : -INFINITY;
                     ov[j][k] = in ? *(const merge_f32x4 *)(ws_o + prow * Dv + d0)
                                   : merge_f32x4{0.f, 0.f, 0.f, 0.f};
@@ -86,8 +92,8 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
         for (int j = 0; j < kUnits; j++) {
             if (!ok[j]) continue;
             const int u = u0 + j * nthr;
-            const int hq = hq0 + u / q4, d0 = (u % q4) * 4;
-            const int64_t row = (int64_t)b * Hq + hq;
+            const int d0 = (u % q4) * 4;
+            const int64_t row = (int64_t)b * Hr + qrow(u);
             merge_bf16x4 ob;
             if (m[j] == -INFINITY) {
                 ob = merge_bf16x4{};
@@ -104,7 +110,8 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
 }
 
 // Fused combine, called by every thread of a workgroup once it has processed all its
-// items [ib, ie) (row group rg: query heads [hq0, hq0 + nrows)).  Release: each thread's
+// items [ib, ie) (row group rg: query heads [hq0, hq0 + nrows) of every query token;
+// `arrivals` workgroups write partials per chunk of the row group).  Release: each thread's
 // partial writes are made visible at device scope (one fence per workgroup), then one
 // thread counts each of the workgroup's partial chunks in; the workgroup that counts a
 // request's last chunk acquires the other workgroups' writes, merges that request, and
@@ -112,9 +119,9 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
 // balanced rule) get out = 0, lse = -inf from workgroup part = b mod num_parts.
 __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *plan, int part,
                                           int ib, int ie, int rg, int n_rowgroups, int hq0,
-                                          int nrows, int *s_flag)
+                                          int nrows, int arrivals, int *s_flag)
 {
-    const int Hq = a.Hkv * a.G;
+    const int Hq = a.Hkv * a.G, nq = a.q_len;
     __threadfence();
     __syncthreads();
     for (int it = ib; it < ie; it++) {
@@ -125,11 +132,11 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
         int32_t *cnt = a.counters + (int64_t)b * n_rowgroups + rg;
         if (threadIdx.x == 0)
             *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                      n - 1;
+                      n * arrivals - 1;
         __syncthreads();
         if (*s_flag) {
             __threadfence();
-            merge_rows<4>(a.ws_o, a.ws_lse, a.out, a.lse, b, c0, n, Hq, a.Dv, hq0, nrows,
+            merge_rows<4>(a.ws_o, a.ws_lse, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0, nrows,
                           threadIdx.x, blockDim.x);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -138,9 +145,9 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
     for (int b = part; b < a.B; b += a.num_parts) {
         if (plan[a.chunk_off_off + b + 1] != plan[a.chunk_off_off + b]) continue;
         const int q4 = a.Dv / 4;
-        for (int u = threadIdx.x; u < nrows * q4; u += blockDim.x) {
-            const int hq = hq0 + u / q4, d0 = (u % q4) * 4;
-            const int64_t row = (int64_t)b * Hq + hq;
+        for (int u = threadIdx.x; u < nq * nrows * q4; u += blockDim.x) {
+            const int rr = u / q4, d0 = (u % q4) * 4;
+            const int64_t row = ((int64_t)b * nq + rr / nrows) * Hq + hq0 + rr % nrows;
             *(merge_bf16x4 *)(a.out + row * a.Dv + d0) = merge_bf16x4{};
             if (d0 == 0) a.lse[row] = -INFINITY;
         }

@@ -229,7 +229,7 @@ def kv_bytes(case: dict) -> int:
 def io_bytes(case: dict) -> int:
     """q, out (bf16), lse (fp32), block table and seq_lens bytes of one step."""
     B, Hkv, G, D, Dv = case["B"], case["Hkv"], case["G"], case["D"], case["Dv"]
-    Hq = Hkv * G
+    R = Hkv * G * case.get("q_len", 1)          # query rows per request
     P = case["page_size"]
     pages = int((-(-np.asarray(case["seq_lens"], np.int64) // P)).sum())
-    return B * Hq * D * 2 + B * Hq * Dv * 2 + B * Hq * 4 + pages * 4 + B * 4
+    return B * R * D * 2 + B * R * Dv * 2 + B * R * 4 + pages * 4 + B * 4

@@ -40,10 +40,11 @@ class GpuRun:
         self.case = case
         self.desc = pb.desc_from_case(case, num_splits, fused=fused)
         self.dev = dev if dev is not None else to_device(case)
-        B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
+        B, Hq, Dv, nq = case["B"], case["Hkv"] * case["G"], case["Dv"], case.get("q_len", 1)
+        lead = (B, Hq) if nq == 1 else (B, nq, Hq)
         self.runner = pb.PagedDecode(self.desc)
-        self.out = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device="cuda")
-        self.lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        self.out = torch.empty(lead + (Dv,), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(lead, dtype=torch.float32, device="cuda")
         if poison:
             self.out.fill_(float("nan"))
             self.lse.fill_(float("nan"))

@@ -60,7 +60,11 @@ BAD = [
     (dict(page_size=8), pb.PA_ERR_UNSUPPORTED),
     (dict(page_size=48), pb.PA_ERR_UNSUPPORTED),
     (dict(G=17), pb.PA_ERR_UNSUPPORTED),
-    (dict(q_len=2), pb.PA_ERR_UNSUPPORTED),
+    (dict(q_len=0), pb.PA_ERR_INVALID),
+    (dict(q_len=65), pb.PA_ERR_UNSUPPORTED),
+    (dict(G=8, q_len=33), pb.PA_ERR_UNSUPPORTED),   # more than 256 query rows per KV head
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
+          q_len=2), pb.PA_ERR_UNSUPPORTED),
     (dict(B=5000), pb.PA_ERR_UNSUPPORTED),
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
      pb.PA_ERR_UNSUPPORTED),
@@ -84,6 +88,15 @@ def test_size_query_fixed_splits_needs_no_device():
     assert pbytes == 4 * (8 + (B * s + 1) + (B + 1) + 4 * B * s + B * 1)
     o = (B * s * 1 * 8 * 64 * 4 + 255) // 256 * 256
     assert wbytes == o + B * s * 1 * 8 * 4
+
+
+def test_size_query_scales_with_query_tokens():
+    # partials are kept per query token: the workspace grows q_len times, the plan not
+    st1, p1, w1 = _plan_status(_desc(num_splits=2))
+    st3, p3, w3 = _plan_status(_desc(num_splits=2, q_len=3))
+    assert st1 == st3 == pb.PA_OK and p1 == p3
+    B, s, rows = 2, 2, 3 * 8
+    assert w3 == (B * s * rows * 64 * 4 + 255) // 256 * 256 + B * s * rows * 4
 
 
 def test_fused_flag_accepted_and_combine_is_launch_free():
