@@ -68,6 +68,10 @@ def lib():
         L.oracle_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
         L.oracle_merge.restype = None
         L.oracle_e4m3_decode_n.argtypes = [vp, vp, ctypes.c_int64]
+        L.oracle_e4m3_encode_n.argtypes = [vp, vp, ctypes.c_int64]
+        L.oracle_kv_append.argtypes = [ctypes.POINTER(_Desc), ctypes.c_int, vp, vp, vp, vp, vp,
+                                       vp, vp, vp]
+        L.oracle_kv_append.restype = ctypes.c_int
         L.oracle_bf16_decode_n.argtypes = [vp, vp, ctypes.c_int64]
         L.oracle_mla656_unpack_n.argtypes = [vp, vp, ctypes.c_int64]
         L.oracle_threads.argtypes = [ctypes.c_int]
@@ -206,6 +210,37 @@ def split_decode(case, items, scale=None, nthreads: int = 0):
         out[b] = O.reshape(rows + (Dv,))
         lse[b] = ls.reshape(rows)
     return out, lse, (m, l, Ot)
+
+
+def kv_append(case, n_new: int, k_new, v_new=None) -> dict:
+    """KV append reference: returns a copy of ``case`` whose pools (and fp8 scale tables)
+    hold the n_new new tokens per request, written at positions seq_lens[b] - n_new + j
+    (seq_lens are the lengths after the append).  k_new, v_new: [B, n_new, Hkv, D] bf16
+    bits (MLA: k_new [B, n_new, 576], v_new None).  See oracle.c for the procedure."""
+    out = dict(case)
+    out["k_pool"] = np.array(case["k_pool"], copy=True)
+    out["v_pool"] = None if case.get("v_pool") is None else np.array(case["v_pool"], copy=True)
+    for key in ("k_scale", "v_scale"):
+        out[key] = None if case.get(key) is None else np.array(case[key], dtype=np.float32, copy=True)
+    kn = _c(k_new, np.uint16)
+    vn = _c(v_new, np.uint16)
+    bt = _c(case["block_table"], np.int32)
+    sl = _c(case["seq_lens"], np.int32)
+    d = _desc(case)
+    rc = lib().oracle_kv_append(ctypes.byref(d), int(n_new), _ptr(kn), _ptr(vn), _ptr(bt), _ptr(sl),
+                                _ptr(out["k_pool"]), _ptr(out["v_pool"]), _ptr(out["k_scale"]),
+                                _ptr(out["v_scale"]))
+    if rc != 0:
+        raise ValueError("a request is shorter than n_new")
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """OCP E4M3FN codes of fp32 values (round to nearest even, saturating at +-448)."""
+    a = _c(x, np.float32)
+    o = np.zeros(a.shape, np.uint8)
+    lib().oracle_e4m3_encode_n(_ptr(a), _ptr(o), a.size)
+    return o
 
 
 def e4m3_decode(codes) -> np.ndarray:

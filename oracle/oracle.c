@@ -391,3 +391,188 @@ void oracle_mla656_unpack_n(const uint8_t *toks, double *k576, int64_t n)
     for (int64_t i = 0; i < n; i++)
         oracle_mla656_unpack(toks + i * 656, k576 + i * 576);
 }
+
+/* ------------------------------------------------------------------------ */
+/* KV append (the step before attention)                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * The new tokens' K/V are written into their pages before attention reads them
+ * (XQA article, section "一次 decode step 的完整时序": the cache already holds the
+ * step's tokens; the append itself happens upstream).  The pages fix no append
+ * procedure for quantised pages, so the following reading is taken:
+ *
+ *  - n_new new tokens per request; seq_lens are the lengths after the append, new
+ *    token j of request b goes to position seq_lens[b] - n_new + j.
+ *  - bf16 pools: plain copy.
+ *  - fp8 page-head pools: one scale per (page, KV head), kept equal to the running
+ *    max|x| / 448 of the values the page has received.  For each page that gets new
+ *    tokens (slots [s0, s1) of it), in position order, with fp32 arithmetic:
+ *        amax  = max |x| over the new values of that page and head
+ *        s0 = 0 (fresh page): scale = amax > 0 ? amax / 448 : 1
+ *        s0 > 0:              scale = max(old scale, amax / 448); when it grows, each
+ *                             older code c of the page is re-encoded as
+ *                             e4m3(fp32(fp32(decode(c) * old) / scale))
+ *        new codes            e4m3(fp32(x / scale))
+ *    K and V have their own scales.
+ *  - MLA 656-byte tokens (FlashMLA walk-through, section 数据加载): per token and
+ *    128-value tile, scale = amax > 0 ? amax / 448 : 1, codes e4m3(fp32(x / scale)),
+ *    the 64 rope values copied as bf16.
+ *  - e4m3(.) is the OCP E4M3FN encoding with round-to-nearest-even, saturating at
+ *    +-448 (the largest finite value; the format has no infinity).
+ */
+
+/* OCP E4M3FN encoding of an fp32 value: round to nearest, ties to even; magnitudes
+   >= 448 give +-448; NaN gives 0x7F.  The representable magnitudes are k * 2^-9 for
+   k < 8 (subnormals) and (8 + m) * 2^(E-3) for m < 8 in the binade [2^E, 2^(E+1)). */
+uint8_t oracle_e4m3_encode(float xf)
+{
+    if (isnan(xf))
+        return 0x7F;
+    const uint8_t s = signbit(xf) ? 0x80 : 0x00;
+    const double a = fabs((double)xf);
+    if (a >= 448.0)
+        return s | 0x7E;
+    int E;
+    if (a < ldexp(1.0, -6)) {
+        E = -6;                      /* subnormal spacing 2^-9 */
+    } else {
+        frexp(a, &E);                /* a = f 2^E', f in [0.5, 1): binade 2^(E'-1) */
+        E -= 1;
+    }
+    const double qstep = ldexp(1.0, E - 3);
+    const double r = rint(a / qstep) * qstep;    /* a / qstep is exact; rint: ties to even */
+    if (r == 0.0)
+        return s;
+    if (r < ldexp(1.0, -6))
+        return s | (uint8_t)(r / ldexp(1.0, -9));
+    int e;
+    const double f = frexp(r, &e);               /* r = (2f) 2^(e-1), 2f in [1, 2) */
+    const int ebits = (e - 1) + 7;
+    const int m = (int)((2.0 * f - 1.0) * 8.0);
+    return s | (uint8_t)(ebits << 3) | (uint8_t)m;
+}
+
+static float bf16_to_f32(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp8 page-head append of one pool (K or V) for request b, KV head h. */
+static void append_fp8_pool(const oracle_desc *d, int n_new, const uint16_t *x_new,
+                            const int32_t *block_table, int b, int h, int L, uint8_t *pool,
+                            float *scales)
+{
+    const int P = d->page_size, D = d->D, Hkv = d->Hkv;
+    const int first = L - n_new;
+    int j = 0;
+    while (j < n_new) {
+        const int pos0 = first + j;
+        const int lp = pos0 / P, s0 = pos0 % P;
+        int s1 = s0;
+        while (j + (s1 - s0) < n_new && s1 < P)
+            s1++;
+        const int64_t page = block_table[(int64_t)b * d->max_pages + lp];
+        float amax = 0.0f;
+        for (int t = 0; t < s1 - s0; t++)
+            for (int i = 0; i < D; i++) {
+                const float v = fabsf(bf16_to_f32(x_new[(((int64_t)b * n_new + j + t) * Hkv + h) * D + i]));
+                if (v > amax)
+                    amax = v;
+            }
+        float *sc = &scales[page * Hkv + h];
+        const float cand = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float scale;
+        if (s0 == 0) {
+            scale = cand;
+        } else {
+            const float old = *sc;
+            const float grown = amax / 448.0f;
+            scale = grown > old ? grown : old;
+            if (scale > old) {
+                for (int t = 0; t < s0; t++) {
+                    uint8_t *row = pool + page * d->s_page + (int64_t)h * d->s_head + (int64_t)t * d->s_tok;
+                    for (int i = 0; i < D; i++) {
+                        const float xo = (float)oracle_e4m3_to_f64(row[i]) * old;
+                        row[i] = oracle_e4m3_encode(xo / scale);
+                    }
+                }
+            }
+        }
+        for (int t = 0; t < s1 - s0; t++) {
+            uint8_t *row = pool + page * d->s_page + (int64_t)h * d->s_head + (int64_t)(s0 + t) * d->s_tok;
+            for (int i = 0; i < D; i++) {
+                const float x = bf16_to_f32(x_new[(((int64_t)b * n_new + j + t) * Hkv + h) * D + i]);
+                row[i] = oracle_e4m3_encode(x / scale);
+            }
+        }
+        *sc = scale;
+        j += s1 - s0;
+    }
+}
+
+/*
+ * Append n_new tokens per request.  k_new, v_new: [B][n_new][Hkv][D] bf16 (MLA:
+ * k_new [B][n_new][576] bf16, v_new unused).  Pools and scale tables are updated in
+ * place.  Returns -1 if a request is shorter than n_new.
+ */
+int oracle_kv_append(const oracle_desc *d, int n_new, const uint16_t *k_new,
+                     const uint16_t *v_new, const int32_t *block_table, const int32_t *seq_lens,
+                     void *k_pool, void *v_pool, float *k_scale, float *v_scale)
+{
+    const int B = d->B, Hkv = d->Hkv, D = d->D, P = d->page_size;
+    for (int b = 0; b < B; b++)
+        if (seq_lens[b] < n_new)
+            return -1;
+    for (int b = 0; b < B; b++) {
+        const int L = seq_lens[b];
+        if (d->kv_format == ORACLE_KV_MLA656) {
+            for (int j = 0; j < n_new; j++) {
+                const int pos = L - n_new + j;
+                const int64_t page = block_table[(int64_t)b * d->max_pages + pos / P];
+                uint8_t *tok = (uint8_t *)k_pool + page * d->s_page + (int64_t)(pos % P) * d->s_tok;
+                const uint16_t *x = k_new + ((int64_t)b * n_new + j) * 576;
+                for (int tile = 0; tile < 4; tile++) {
+                    float amax = 0.0f;
+                    for (int i = 0; i < 128; i++) {
+                        const float v = fabsf(bf16_to_f32(x[128 * tile + i]));
+                        if (v > amax)
+                            amax = v;
+                    }
+                    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+                    for (int i = 0; i < 128; i++)
+                        tok[128 * tile + i] = oracle_e4m3_encode(bf16_to_f32(x[128 * tile + i]) / scale);
+                    memcpy(tok + 512 + 4 * tile, &scale, 4);
+                }
+                for (int r = 0; r < 64; r++) {
+                    tok[528 + 2 * r] = (uint8_t)(x[512 + r] & 0xFF);
+                    tok[528 + 2 * r + 1] = (uint8_t)(x[512 + r] >> 8);
+                }
+            }
+            continue;
+        }
+        for (int h = 0; h < Hkv; h++) {
+            if (d->kv_format == ORACLE_KV_BF16) {
+                for (int j = 0; j < n_new; j++) {
+                    const int pos = L - n_new + j;
+                    const int64_t page = block_table[(int64_t)b * d->max_pages + pos / P];
+                    const int64_t off = page * d->s_page + (int64_t)h * d->s_head + (int64_t)(pos % P) * d->s_tok;
+                    memcpy((uint16_t *)k_pool + off, k_new + (((int64_t)b * n_new + j) * Hkv + h) * D, 2 * (size_t)D);
+                    memcpy((uint16_t *)v_pool + off, v_new + (((int64_t)b * n_new + j) * Hkv + h) * D, 2 * (size_t)D);
+                }
+            } else {
+                append_fp8_pool(d, n_new, k_new, block_table, b, h, L, (uint8_t *)k_pool, k_scale);
+                append_fp8_pool(d, n_new, v_new, block_table, b, h, L, (uint8_t *)v_pool, v_scale);
+            }
+        }
+    }
+    return 0;
+}
+
+void oracle_e4m3_encode_n(const float *x, uint8_t *codes, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        codes[i] = oracle_e4m3_encode(x[i]);
+}

@@ -43,6 +43,12 @@ int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
 void oracle_merge(int n, int rows, int Dv, const double *m, const double *l, const double *Ot,
                   double *O, double *lse);
 
+uint8_t oracle_e4m3_encode(float x);
+void oracle_e4m3_encode_n(const float *x, uint8_t *codes, int64_t n);
+int oracle_kv_append(const oracle_desc *d, int n_new, const uint16_t *k_new,
+                     const uint16_t *v_new, const int32_t *block_table, const int32_t *seq_lens,
+                     void *k_pool, void *v_pool, float *k_scale, float *v_scale);
+
 void oracle_e4m3_decode_n(const uint8_t *codes, double *out, int64_t n);
 void oracle_bf16_decode_n(const uint16_t *bits, double *out, int64_t n);
 void oracle_mla656_unpack_n(const uint8_t *toks, double *k576, int64_t n);
