@@ -166,6 +166,31 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
 pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
                             void *out, float *lse, void *stream);
 
+/*
+ * KV append: writes n_new new tokens per request into their pages, the step before
+ * attention (XQA article, section "一次 decode step 的完整时序": attention reads a
+ * cache that already holds the step's K/V).  seq_lens[b] (device) is the length AFTER
+ * the append; new token j of request b goes to position seq_lens[b] - n_new + j, whose
+ * page block_table[b][pos / page_size] the caller has already assigned.
+ *   k_new, v_new  [B][n_new][Hkv][D] bf16, 16-byte aligned (PA_KV_MLA656: k_new
+ *                 [B][n_new][576] bf16, v_new and v_pool NULL)
+ *   k_pool, v_pool  written in place; k_scale, v_scale [num_pages][Hkv] fp32, read and
+ *                 written (PA_KV_FP8_E4M3_PAGE_HEAD), else NULL
+ * PA_KV_BF16: plain copy.  PA_KV_FP8_E4M3_PAGE_HEAD: each (page, KV head) scale is the
+ * running max|x| / 448 of the values the page has received.  A page whose first slot
+ * receives a new token starts fresh (scale = amax / 448 of its new values, 1 if all are
+ * 0); otherwise scale = max(old, amax / 448), and when it grows the page's older codes
+ * are re-encoded with it (e4m3(fp32(fp32(decode(c) * old) / scale)), one more rounding
+ * each).  Codes are OCP E4M3FN, round to nearest even, saturating at +-448.
+ * PA_KV_MLA656: per token, one scale per 128-value tile = max|x| / 448 (1 if 0), codes
+ * e4m3(fp32(x / scale)), the 64 rope values copied as bf16.
+ * Pages that receive new tokens must belong to a single request; requests with
+ * seq_lens[b] < n_new are skipped.  n_new <= 65535.
+ */
+pa_status pa_kv_append(const pa_decode_desc *desc, int32_t n_new, const void *k_new,
+                       const void *v_new, const int32_t *block_table, const int32_t *seq_lens,
+                       void *k_pool, void *v_pool, float *k_scale, float *v_scale, void *stream);
+
 /* Number of workgroups along the part axis that pa_decode_run launches for `desc`
    on the current device (B * num_splits, or the balanced part count). */
 pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts);

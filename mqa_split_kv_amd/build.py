@@ -22,7 +22,7 @@ LIB = os.path.join(LIBDIR, "libpa_decode.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["pa_api.cpp", "pa_plan.hip", "pa_decode_kernel.hip", "pa_mla_kernel.hip",
-           "pa_combine.hip"]
+           "pa_combine.hip", "pa_append.hip"]
 PROBE_SOURCES = ["pa_probe.hip"]
 PROBE_LIB = os.path.join(LIBDIR, "libpa_probe.so")
 ARCH = "gfx950"

@@ -13,6 +13,7 @@ using pa::PlanLayout;
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxQLen = 64;
+constexpr int kMaxAppendTokens = 65535;     // grid y of the MLA append
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device (queried once per device).
@@ -124,6 +125,29 @@ const char *pa_status_string(pa_status s)
     case PA_ERR_DEVICE: return "HIP device error";
     }
     return "unknown status";
+}
+
+pa_status pa_kv_append(const pa_decode_desc *desc, int32_t n_new, const void *k_new,
+                       const void *v_new, const int32_t *block_table, const int32_t *seq_lens,
+                       void *k_pool, void *v_pool, float *k_scale, float *v_scale, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    if (n_new <= 0) return PA_ERR_INVALID;
+    if (n_new > kMaxAppendTokens) return PA_ERR_UNSUPPORTED;
+    const bool mla = desc->kv_format == PA_KV_MLA656;
+    const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
+    if (!k_new || !block_table || !seq_lens || !k_pool) return PA_ERR_INVALID;
+    if (mla ? (v_new != nullptr || v_pool != nullptr) : (!v_new || !v_pool)) return PA_ERR_INVALID;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(k_pool) || (!mla && (!aligned16(v_new) || !aligned16(v_pool))) ||
+        ((uintptr_t)block_table & 3) || ((uintptr_t)seq_lens & 3) || ((uintptr_t)k_scale & 3) ||
+        ((uintptr_t)v_scale & 3))
+        return PA_ERR_INVALID;
+    if (pa::launch_append(desc, n_new, k_new, v_new, block_table, seq_lens, k_pool, v_pool,
+                          k_scale, v_scale, (hipStream_t)stream) != hipSuccess)
+        return PA_ERR_DEVICE;
+    return PA_OK;
 }
 
 pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts)

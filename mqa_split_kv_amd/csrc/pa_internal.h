@@ -95,6 +95,9 @@ hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout 
                        int num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_append(const pa_decode_desc *d, int n_new, const void *k_new, const void *v_new,
+                         const int32_t *block_table, const int32_t *seq_lens, void *k_pool,
+                         void *v_pool, float *k_scale, float *v_scale, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           uint16_t *out, float *lse, int B, int Hkv, int G, int q_len, int Dv,
                           int chunk_off_off, hipStream_t stream);

@@ -147,3 +147,24 @@ def test_plan_size_check():
                           ctypes.c_void_p(ctypes.addressof(buf)), ctypes.byref(small),
                           ctypes.byref(wb), None)
     assert st == pb.PA_ERR_SIZE
+
+
+def test_append_rejects_bad_arguments_on_host():
+    L = pb.lib()
+    buf = ctypes.create_string_buffer(1 << 12)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    p = ctypes.c_void_p
+    d = _desc()
+    args = [p(base)] * 6 + [None, None, None]
+    assert L.pa_kv_append(ctypes.byref(d), 0, *args) == pb.PA_ERR_INVALID          # n_new = 0
+    assert L.pa_kv_append(ctypes.byref(d), 70000, *args) == pb.PA_ERR_UNSUPPORTED
+    assert L.pa_kv_append(ctypes.byref(d), 1, None, *[p(base)] * 5, None, None,
+                          None) == pb.PA_ERR_INVALID                                 # no k_new
+    assert L.pa_kv_append(ctypes.byref(d), 1, p(base + 8), *[p(base)] * 5, None, None,
+                          None) == pb.PA_ERR_INVALID                                 # misaligned
+    d8 = _desc(kv_format=pb.PA_KV_FP8_E4M3_PAGE_HEAD)
+    assert L.pa_kv_append(ctypes.byref(d8), 1, *[p(base)] * 6, None, None,
+                          None) == pb.PA_ERR_INVALID                                 # no scales
+    dm = _desc(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16)
+    assert L.pa_kv_append(ctypes.byref(dm), 1, *[p(base)] * 6, None, None,
+                          None) == pb.PA_ERR_INVALID                                 # v_new given
