@@ -34,6 +34,7 @@ class _Desc(ctypes.Structure):
         ("max_pages", ctypes.c_int32),
         ("s_page", ctypes.c_int64), ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64),
         ("kv_format", ctypes.c_int32), ("q_len", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("topk", ctypes.c_int32),
     ]
 
 
@@ -58,10 +59,10 @@ def lib():
             build(force=False)
         L = ctypes.CDLL(_LIB_PATH)
         vp = ctypes.c_void_p
-        L.oracle_decode.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp,
+        L.oracle_decode.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_double, vp, vp, vp, ctypes.c_int]
         L.oracle_decode.restype = ctypes.c_int
-        L.oracle_ranges.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp,
+        L.oracle_ranges.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_double, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_int]
         L.oracle_ranges.restype = ctypes.c_int
@@ -96,7 +97,8 @@ def _c(a, dtype=None):
 def _desc(case) -> _Desc:
     return _Desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
                  case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
-                 case["s_tok"], case["kv_format"], case.get("q_len", 1))
+                 case["s_tok"], case["kv_format"], case.get("q_len", 1), case.get("window", 0),
+                 case.get("topk", 0))
 
 
 def _arrays(case):
@@ -124,6 +126,8 @@ def _rows_shape(case):
 def decode(case, scale=None, pairs=None, nthreads: int = 0):
     """Plain definition for every (b, h) pair (or the boolean mask ``pairs`` [B, Hkv]).
 
+    Optional case keys: ``window`` (sliding window), ``sinks`` ([Hq] float32 sink
+    logits), ``topk`` and ``indices`` ([B, topk] int32 key positions, sparse).
     Returns (out [B, Hq, Dv] float64, lse [B, Hq] float64) - with q_len > 1 query
     tokens per request, out [B, q_len, Hq, Dv] and lse [B, q_len, Hq]; rows of skipped
     pairs are NaN.
@@ -136,8 +140,11 @@ def decode(case, scale=None, pairs=None, nthreads: int = 0):
     out = np.full(_rows_shape(case) + (Dv,), np.nan)
     lse = np.full(_rows_shape(case), np.nan)
     d = _desc(case)
+    idx = _c(case.get("indices"), np.int32)
+    sinks = _c(case.get("sinks"), np.float32)
     rc = lib().oracle_decode(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
-                             _ptr(bt), _ptr(sl), sc, _ptr(mask), _ptr(out), _ptr(lse), nthreads)
+                             _ptr(bt), _ptr(sl), _ptr(idx), _ptr(sinks), sc, _ptr(mask), _ptr(out),
+                             _ptr(lse), nthreads)
     if rc != 0:
         raise MemoryError("oracle_decode failed")
     return out, lse
@@ -146,7 +153,8 @@ def decode(case, scale=None, pairs=None, nthreads: int = 0):
 def ranges(case, rb, rt0, rt1, scale=None, nthreads: int = 0):
     """Partial triples (m, l, Ot) of the XQA multi-block merge for token ranges.
 
-    rb, rt0, rt1: request index and [begin, end) token range of each range.
+    rb, rt0, rt1: request index and [begin, end) token range of each range (sparse:
+    range of index slots).  Sinks are not part of partials.
     Returns m, l [n, Hkv, G] and Ot [n, Hkv, G, Dv] (unnormalised), float64; with
     q_len > 1 query tokens, [n, q_len, Hkv, G] and [n, q_len, Hkv, G, Dv].
     """
@@ -162,9 +170,10 @@ def ranges(case, rb, rt0, rt1, scale=None, nthreads: int = 0):
     Ot = np.zeros(lead + (Dv,))
     sc = float(case["scale"] if scale is None else scale)
     d = _desc(case)
+    idx = _c(case.get("indices"), np.int32)
     rc = lib().oracle_ranges(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(ks), _ptr(vs),
-                             _ptr(bt), _ptr(sl), sc, n, _ptr(rb), _ptr(rt0), _ptr(rt1), _ptr(m),
-                             _ptr(l), _ptr(Ot), nthreads)
+                             _ptr(bt), _ptr(sl), _ptr(idx), sc, n, _ptr(rb), _ptr(rt0), _ptr(rt1),
+                             _ptr(m), _ptr(l), _ptr(Ot), nthreads)
     if rc != 0:
         raise MemoryError("oracle_ranges failed")
     return m, l, Ot
@@ -202,11 +211,20 @@ def split_decode(case, items, scale=None, nthreads: int = 0):
     rows = _rows_shape(case)[1:]
     out = np.zeros((B,) + rows + (Dv,))
     lse = np.full((B,) + rows, -np.inf)
+    sinks = case.get("sinks")
     for b in range(B):
         sel = np.nonzero(rb == b)[0]
-        if sel.size == 0:
+        mb, lb, ob = m[sel], l[sel], Ot[sel]
+        if sinks is not None:
+            # the sink joins the merge once per request, as a partial (sink, 1, 0)
+            srow = np.broadcast_to(np.asarray(sinks, np.float64).reshape(
+                (1,) * (mb.ndim - 2) + (case["Hkv"], case["G"])), (1,) + mb.shape[1:])
+            mb = np.concatenate([mb, srow])
+            lb = np.concatenate([lb, np.ones((1,) + lb.shape[1:])])
+            ob = np.concatenate([ob, np.zeros((1,) + ob.shape[1:])])
+        if mb.shape[0] == 0:
             continue
-        O, ls = merge(m[sel], l[sel], Ot[sel])
+        O, ls = merge(mb, lb, ob)
         out[b] = O.reshape(rows + (Dv,))
         lse[b] = ls.reshape(rows)
     return out, lse, (m, l, Ot)

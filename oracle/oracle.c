@@ -29,6 +29,21 @@
  * itself: query token i (0-based) attends to tokens [0, L - q_len + i + 1).  q is
  * [B][q_len][Hq][D], out [B][q_len][Hq][Dv], lse [B][q_len][Hq].
  *
+ * Variants on the same definition (readings of the pages, which name these without
+ * formulas):
+ *  - sliding window W > 0 (XQA article, section "分页 KV: 页号怎么变成 TMA 坐标": the
+ *    window only looks at the last W tokens, so leading pages are skipped): the query
+ *    token at position p attends to [max(0, p - W + 1), p + 1).
+ *  - attention sink (XQA article, section "一个容易漏掉的细节: attention sink"): a
+ *    per-query-head logit sink[hq], in the units of scale * q . k, that joins the
+ *    softmax denominator once and carries no value: out = sum_t e^{s_t} v_t /
+ *    (e^{sink} + sum_t e^{s_t}) and lse = ln(e^{sink} + sum_t e^{s_t}).  It is the
+ *    merge of one more partial (m = sink, l = 1, O = 0), the form used below.
+ *  - sparse top-k (FlashMLA walk-through, section 调度: the decode call takes sparse
+ *    indices): one query token per request, which attends to the key positions
+ *    indices[b][0 .. topk) of its request; entries outside [0, L) are skipped and a
+ *    position listed twice counts twice.
+ *
  * Pins: see tests/test_oracle.py (dense library attention, closed forms,
  * invariances, the rescale worked example, all 256 e4m3 codes).
  */
@@ -166,9 +181,12 @@ static void fetch(const oracle_desc *d, const void *k_pool, const void *v_pool,
 static int range_state(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                        const void *v_pool, const float *k_scale, const float *v_scale,
                        const int32_t *block_table, double scale, int b, int h, int qi, int t0,
-                       int t1, double *m, double *l, double *Ot)
+                       int t1, int tlo, const int32_t *idx, int L, double *m, double *l,
+                       double *Ot)
 {
     const int G = d->G, D = d->D, Dv = d->Dv;
+    if (!idx && t0 < tlo)
+        t0 = tlo;
     const int n = t1 > t0 ? t1 - t0 : 0;
     for (int g = 0; g < G; g++) {
         m[g] = -INFINITY;
@@ -194,29 +212,39 @@ static int range_state(const oracle_desc *d, const uint16_t *q, const void *k_po
             qf[(int64_t)g * D + i] = oracle_bf16_to_f64(
                 q[(((int64_t)b * d->q_len + qi) * Hq + (int64_t)h * G + g) * D + i]);
 
+    /* token of range slot u: position t0 + u, or the listed position idx[t0 + u] (sparse;
+       -1 when it lies outside the request) */
+#define RANGE_TOKEN(u) (idx ? ((idx[t0 + (u)] >= 0 && idx[t0 + (u)] < L) ? idx[t0 + (u)] : -1) : t0 + (u))
     /* pass 1: logits */
-    for (int t = t0; t < t1; t++) {
+    for (int u = 0; u < n; u++) {
+        const int t = RANGE_TOKEN(u);
+        if (t < 0)
+            continue;
         fetch(d, k_pool, v_pool, k_scale, v_scale, block_table, b, h, t, 0, x);
         for (int g = 0; g < G; g++) {
             double acc = 0.0;
             for (int i = 0; i < D; i++)
                 acc += qf[(int64_t)g * D + i] * x[i];
             double st = scale * acc;
-            s[(int64_t)g * n + (t - t0)] = st;
+            s[(int64_t)g * n + u] = st;
             if (st > m[g])
                 m[g] = st;
         }
     }
     /* pass 2: weights, denominator, weighted values */
-    for (int t = t0; t < t1; t++) {
+    for (int u = 0; u < n; u++) {
+        const int t = RANGE_TOKEN(u);
+        if (t < 0)
+            continue;
         fetch(d, k_pool, v_pool, k_scale, v_scale, block_table, b, h, t, 1, x);
         for (int g = 0; g < G; g++) {
-            double w = exp(s[(int64_t)g * n + (t - t0)] - m[g]);
+            double w = exp(s[(int64_t)g * n + u] - m[g]);
             l[g] += w;
             for (int i = 0; i < Dv; i++)
                 Ot[(int64_t)g * Dv + i] += w * x[i];
         }
     }
+#undef RANGE_TOKEN
     free(qf);
     free(s);
     free(x);
@@ -248,6 +276,15 @@ static int causal_limit(const oracle_desc *d, int L, int qi)
     return lim > 0 ? lim : 0;
 }
 
+/* First token query token qi sees under the sliding window (0 without one). */
+static int window_start(const oracle_desc *d, int L, int qi)
+{
+    if (d->window <= 0)
+        return 0;
+    const int lo = L - d->q_len + qi - d->window + 1;
+    return lo > 0 ? lo : 0;
+}
+
 /*
  * Whole-request attention for every (b, h) with pair_mask[b*Hkv+h] != 0
  * (pair_mask NULL: all pairs):  out = Ot / l,  lse = m + ln l, for each query token.
@@ -256,10 +293,13 @@ static int causal_limit(const oracle_desc *d, int L, int qi)
  */
 int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, const int32_t *seq_lens, double scale,
-                  const uint8_t *pair_mask, double *out, double *lse, int nthreads)
+                  const int32_t *block_table, const int32_t *seq_lens, const int32_t *indices,
+                  const float *sinks, double scale, const uint8_t *pair_mask, double *out,
+                  double *lse, int nthreads)
 {
     const int B = d->B, Hkv = d->Hkv, G = d->G, Dv = d->Dv, Hq = Hkv * G, nq = d->q_len;
+    if (d->topk > 0 && (nq != 1 || !indices))
+        return -1;
     int err = 0;
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
@@ -271,14 +311,35 @@ int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
         double *m = (double *)malloc(sizeof(double) * (size_t)G);
         double *l = (double *)malloc(sizeof(double) * (size_t)G);
         double *Ot = (double *)malloc(sizeof(double) * (size_t)G * Dv);
-        if (!m || !l || !Ot ||
-            range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h, qi, 0,
-                        causal_limit(d, seq_lens[b], qi), m, l, Ot) != 0) {
+        const int L = seq_lens[b];
+        int rc = -1;
+        if (m && l && Ot) {
+            if (d->topk > 0)
+                rc = range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h,
+                                 qi, 0, d->topk, 0, indices + (int64_t)b * d->topk, L, m, l, Ot);
+            else
+                rc = range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, b, h,
+                                 qi, 0, causal_limit(d, L, qi), window_start(d, L, qi), NULL, L,
+                                 m, l, Ot);
+        }
+        if (rc != 0) {
             err |= 1;
         } else {
             for (int g = 0; g < G; g++) {
                 const int64_t row = ((int64_t)b * nq + qi) * Hq + (int64_t)h * G + g;
-                if (l[g] > 0.0) {
+                if (sinks) {
+                    /* merge with the sink's partial (m = sink, l = 1, O = 0) */
+                    const double ms[2] = {m[g], (double)sinks[h * G + g]};
+                    const double ls[2] = {l[g], 1.0};
+                    double *ot2 = (double *)calloc(2 * (size_t)Dv, sizeof(double));
+                    if (!ot2) {
+                        err |= 1;
+                        continue;
+                    }
+                    memcpy(ot2, Ot + (int64_t)g * Dv, sizeof(double) * (size_t)Dv);
+                    oracle_merge(2, 1, Dv, ms, ls, ot2, out + row * Dv, lse + row);
+                    free(ot2);
+                } else if (l[g] > 0.0) {
                     for (int i = 0; i < Dv; i++)
                         out[row * Dv + i] = Ot[(int64_t)g * Dv + i] / l[g];
                     lse[row] = m[g] + log(l[g]);
@@ -304,12 +365,14 @@ int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
  */
 int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, const int32_t *seq_lens, double scale, int n,
-                  const int32_t *rb, const int32_t *rt0, const int32_t *rt1, double *m,
-                  double *l, double *Ot, int nthreads)
+                  const int32_t *block_table, const int32_t *seq_lens, const int32_t *indices,
+                  double scale, int n, const int32_t *rb, const int32_t *rt0, const int32_t *rt1,
+                  double *m, double *l, double *Ot, int nthreads)
 {
     const int Hkv = d->Hkv, G = d->G, Dv = d->Dv, nq = d->q_len;
-    if (nq > 1 && !seq_lens)
+    if ((nq > 1 || d->window > 0 || d->topk > 0) && !seq_lens)
+        return -1;
+    if (d->topk > 0 && !indices)
         return -1;
     int err = 0;
     set_threads(nthreads);
@@ -317,14 +380,18 @@ int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
     for (int64_t pr = 0; pr < (int64_t)n * nq * Hkv; pr++) {
         const int i = (int)(pr / ((int64_t)nq * Hkv));
         const int qi = (int)((pr / Hkv) % nq), h = (int)(pr % Hkv);
-        int t1 = rt1[i];
-        if (nq > 1) {
-            const int lim = causal_limit(d, seq_lens[rb[i]], qi);
+        int t1 = rt1[i], tlo = 0;
+        const int L = seq_lens ? seq_lens[rb[i]] : 0;
+        const int32_t *idx = d->topk > 0 ? indices + (int64_t)rb[i] * d->topk : NULL;
+        if (!idx && seq_lens) {
+            const int lim = causal_limit(d, L, qi);
             if (t1 > lim)
                 t1 = lim;
+            tlo = window_start(d, L, qi);
         }
         if (range_state(d, q, k_pool, v_pool, k_scale, v_scale, block_table, scale, rb[i], h, qi,
-                        rt0[i], t1, m + pr * G, l + pr * G, Ot + pr * (int64_t)G * Dv) != 0)
+                        rt0[i], t1, tlo, idx, L, m + pr * G, l + pr * G,
+                        Ot + pr * (int64_t)G * Dv) != 0)
             err |= 1;
     }
     return err ? -1 : 0;

@@ -20,6 +20,8 @@ typedef struct {
     int64_t s_page, s_head, s_tok;
     int32_t kv_format;
     int32_t q_len;   /* query tokens per request (1: plain decode) */
+    int32_t window;  /* sliding window in tokens (0: off) */
+    int32_t topk;    /* sparse: key positions per request listed in `indices` (0: dense) */
 } oracle_desc;
 
 double oracle_bf16_to_f64(uint16_t bits);
@@ -30,13 +32,14 @@ int oracle_threads(int nthreads);
 
 int oracle_decode(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, const int32_t *seq_lens, double scale,
-                  const uint8_t *pair_mask, double *out, double *lse, int nthreads);
+                  const int32_t *block_table, const int32_t *seq_lens, const int32_t *indices,
+                  const float *sinks, double scale, const uint8_t *pair_mask, double *out,
+                  double *lse, int nthreads);
 
 int oracle_ranges(const oracle_desc *d, const uint16_t *q, const void *k_pool,
                   const void *v_pool, const float *k_scale, const float *v_scale,
-                  const int32_t *block_table, const int32_t *seq_lens, double scale, int n,
-                  const int32_t *rb,
+                  const int32_t *block_table, const int32_t *seq_lens, const int32_t *indices,
+                  double scale, int n, const int32_t *rb,
                   const int32_t *rt0, const int32_t *rt1, double *m, double *l, double *Ot,
                   int nthreads);
 
