@@ -107,6 +107,13 @@ typedef struct {
     int32_t num_splits;        /* 0: balanced split scheduling; s > 0: s chunks per request */
     int32_t kv_format;         /* pa_kv_format */
     int32_t flags;             /* 0 or PA_FLAG_FUSED_COMBINE; other bits: PA_ERR_INVALID */
+    int32_t window;            /* sliding window W > 0: the query token at position p sees
+                                  keys [max(0, p - W + 1), p]; tiles before the window are
+                                  never read (XQA article, section "分页 KV: 页号怎么变成
+                                  TMA 坐标").  0: off */
+    int32_t topk;              /* sparse decode (PA_KV_MLA656, q_len 1, no window): each
+                                  request attends to the topk key positions listed in
+                                  `indices` (FlashMLA walk-through, section 调度).  0: off */
 } pa_decode_desc;
 
 /*
@@ -138,6 +145,14 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
  *   k_scale, v_scale  [num_pages][Hkv] fp32 for PA_KV_FP8_E4M3_PAGE_HEAD, else NULL
  *   block_table [B][max_pages_per_seq] int32; seq_lens [B] int32 (must be the values
  *               the plan was built from)
+ *   indices     desc->topk > 0: [B][topk] int32 key positions per request; entries
+ *               outside [0, seq_lens[b]) are skipped, a position listed twice counts
+ *               twice.  Else NULL.
+ *   sinks       [Hkv * G] fp32 attention-sink logits (units of scale * q . k) or NULL.
+ *               A sink joins the softmax denominator once and carries no value (XQA
+ *               article, section "一个容易漏掉的细节: attention sink"): out = sum_t
+ *               e^{s_t} v_t / (e^{sink} + sum_t e^{s_t}), lse = ln(e^{sink} + sum_t e^{s_t}).
+ *               Pass the same pointer to pa_decode_combine.
  *   scale       logit scale; <= 0 selects 1/sqrt(D)
  *   out         [B][Hq][Dv] bf16; lse [B][Hq] fp32 (natural log)
  *   plan        written by pa_decode_plan for the same desc (flags may differ).  With
@@ -152,19 +167,20 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
 pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
                         const void *k_pool, const void *v_pool, const float *k_scale,
                         const float *v_scale, const int32_t *block_table,
-                        const int32_t *seq_lens, float scale, void *out, float *lse,
-                        void *workspace, void *stream);
+                        const int32_t *seq_lens, const int32_t *indices, const float *sinks,
+                        float scale, void *out, float *lse, void *workspace, void *stream);
 
 /*
  * Combine.  For every request cut into several chunks (and every request of length
  * 0) merges the chunk partials: M = max_i lse_i, lse = M + ln sum_i exp(lse_i - M),
  * out = sum_i exp(lse_i - lse) * O_i (XQA article, section "归约怎么记", merge
  * equation, written for normalised partials).  Requests done in one chunk are left
- * as pa_decode_run wrote them.  A no-op launch-free call when num_splits == 1 or the
+ * as pa_decode_run wrote them.  sinks: the pointer given to pa_decode_run (its sink
+ * joins each merged row once).  A no-op launch-free call when num_splits == 1 or the
  * desc has PA_FLAG_FUSED_COMBINE.
  */
 pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
-                            void *out, float *lse, void *stream);
+                            const float *sinks, void *out, float *lse, void *stream);
 
 /*
  * KV append: writes n_new new tokens per request into their pages, the step before

@@ -31,6 +31,7 @@ class PaDecodeDesc(ctypes.Structure):
         ("s_page", ctypes.c_int64), ("s_head", ctypes.c_int64), ("s_tok", ctypes.c_int64),
         ("q_len", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("kv_format", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("topk", ctypes.c_int32),
     ]
 
 
@@ -52,9 +53,9 @@ def lib() -> ctypes.CDLL:
         vp, dp = ctypes.c_void_p, ctypes.POINTER(PaDecodeDesc)
         szp = ctypes.POINTER(ctypes.c_size_t)
         L.pa_decode_plan.argtypes = [dp, vp, vp, szp, szp, vp]
-        L.pa_decode_run.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
-                                    vp, vp]
-        L.pa_decode_combine.argtypes = [dp, vp, vp, vp, vp, vp]
+        L.pa_decode_run.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                    vp, vp, vp, vp]
+        L.pa_decode_combine.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         L.pa_kv_append.argtypes = [dp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_decode_num_parts.argtypes = [dp, ctypes.POINTER(ctypes.c_int32)]
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -71,9 +72,10 @@ def status_string(s: int) -> str:
 
 
 def make_desc(B, Hkv, G, D, Dv, page_size, num_pages, max_pages_per_seq, s_page, s_head,
-              s_tok, num_splits=0, kv_format=PA_KV_BF16, q_len=1, flags=0) -> PaDecodeDesc:
+              s_tok, num_splits=0, kv_format=PA_KV_BF16, q_len=1, flags=0, window=0,
+              topk=0) -> PaDecodeDesc:
     return PaDecodeDesc(B, Hkv, G, D, Dv, page_size, num_pages, max_pages_per_seq, s_page,
-                        s_head, s_tok, q_len, num_splits, kv_format, flags)
+                        s_head, s_tok, q_len, num_splits, kv_format, flags, window, topk)
 
 
 def desc_from_case(case: dict, num_splits: Optional[int] = None,
@@ -83,7 +85,8 @@ def desc_from_case(case: dict, num_splits: Optional[int] = None,
     return make_desc(case["B"], case["Hkv"], case["G"], case["D"], case["Dv"], case["page_size"],
                      case["num_pages"], case["max_pages"], case["s_page"], case["s_head"],
                      case["s_tok"], ns, case["kv_format"], q_len=case.get("q_len", 1),
-                     flags=PA_FLAG_FUSED_COMBINE if fused else 0)
+                     flags=PA_FLAG_FUSED_COMBINE if fused else 0, window=case.get("window", 0),
+                     topk=case.get("topk", 0))
 
 
 def _p(t):
@@ -113,17 +116,18 @@ def pa_decode_plan(desc: PaDecodeDesc, seq_lens=None, plan=None, stream=None):
 
 
 def pa_decode_run(desc: PaDecodeDesc, plan, q, k_pool, v_pool, k_scale, v_scale, block_table,
-                  seq_lens, scale: float, out, lse, workspace, stream=None):
+                  seq_lens, scale: float, out, lse, workspace, stream=None, indices=None,
+                  sinks=None):
     st = lib().pa_decode_run(ctypes.byref(desc), _p(plan), _p(q), _p(k_pool), _p(v_pool),
                              _p(k_scale), _p(v_scale), _p(block_table), _p(seq_lens),
-                             ctypes.c_float(scale), _p(out), _p(lse), _p(workspace),
-                             _stream(stream))
+                             _p(indices), _p(sinks), ctypes.c_float(scale), _p(out), _p(lse),
+                             _p(workspace), _stream(stream))
     _check("pa_decode_run", st)
 
 
-def pa_decode_combine(desc: PaDecodeDesc, plan, workspace, out, lse, stream=None):
-    st = lib().pa_decode_combine(ctypes.byref(desc), _p(plan), _p(workspace), _p(out), _p(lse),
-                                 _stream(stream))
+def pa_decode_combine(desc: PaDecodeDesc, plan, workspace, out, lse, stream=None, sinks=None):
+    st = lib().pa_decode_combine(ctypes.byref(desc), _p(plan), _p(workspace), _p(sinks), _p(out),
+                                 _p(lse), _stream(stream))
     _check("pa_decode_combine", st)
 
 
@@ -155,17 +159,17 @@ class PagedDecode:
         pa_decode_plan(self.desc, seq_lens, self.plan_t, stream)
 
     def run(self, q, k_pool, v_pool, block_table, seq_lens, out, lse, k_scale=None,
-            v_scale=None, scale: float = 0.0, stream=None):
+            v_scale=None, scale: float = 0.0, stream=None, indices=None, sinks=None):
         pa_decode_run(self.desc, self.plan_t, q, k_pool, v_pool, k_scale, v_scale, block_table,
-                      seq_lens, scale, out, lse, self.ws, stream)
+                      seq_lens, scale, out, lse, self.ws, stream, indices=indices, sinks=sinks)
 
-    def combine(self, out, lse, stream=None):
-        pa_decode_combine(self.desc, self.plan_t, self.ws, out, lse, stream)
+    def combine(self, out, lse, stream=None, sinks=None):
+        pa_decode_combine(self.desc, self.plan_t, self.ws, out, lse, stream, sinks=sinks)
 
     def __call__(self, *args, **kw):
         self.run(*args, **kw)
         self.combine(kw["out"] if "out" in kw else args[5], kw["lse"] if "lse" in kw else args[6],
-                     kw.get("stream"))
+                     kw.get("stream"), sinks=kw.get("sinks"))
 
 
 def default_scale(D: int) -> float:

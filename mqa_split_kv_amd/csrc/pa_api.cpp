@@ -53,6 +53,10 @@ pa_status check_desc(const pa_decode_desc *d)
     if ((d->s_page * eb) % 16 || (d->s_head * eb) % 16 || (d->s_tok * eb) % 16) return PA_ERR_INVALID;
     if ((int64_t)d->Hkv * d->G > 65536) return PA_ERR_UNSUPPORTED;
     if (d->q_len > kMaxQLen) return PA_ERR_UNSUPPORTED;
+    if (d->window < 0 || d->topk < 0) return PA_ERR_INVALID;
+    if (d->topk > 0 && (d->kv_format != PA_KV_MLA656 || d->window > 0 || d->q_len != 1))
+        return PA_ERR_UNSUPPORTED;     // sparse decode: MLA tokens, one query token
+    if (d->topk > (1 << 24)) return PA_ERR_UNSUPPORTED;
     const int P = d->page_size;
     if (P != 16 && P != 32 && P != 64 && P != 128 && P != 256) return PA_ERR_UNSUPPORTED;
     if (d->B > pa::kMaxBatch) return PA_ERR_UNSUPPORTED;
@@ -181,8 +185,7 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
     if (((uintptr_t)plan & 3) || ((uintptr_t)seq_lens & 3)) return PA_ERR_INVALID;
     if (*plan_bytes < pbytes) return PA_ERR_SIZE;
     if (workspace_bytes) *workspace_bytes = wbytes;
-    if (pa::launch_plan(seq_lens, (int32_t *)plan, L, desc->num_splits, (hipStream_t)stream) !=
-        hipSuccess)
+    if (pa::launch_plan(seq_lens, (int32_t *)plan, L, desc, (hipStream_t)stream) != hipSuccess)
         return PA_ERR_DEVICE;
     return PA_OK;
 }
@@ -190,13 +193,15 @@ pa_status pa_decode_plan(const pa_decode_desc *desc, const int32_t *seq_lens, vo
 pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
                         const void *k_pool, const void *v_pool, const float *k_scale,
                         const float *v_scale, const int32_t *block_table,
-                        const int32_t *seq_lens, float scale, void *out, float *lse,
-                        void *workspace, void *stream)
+                        const int32_t *seq_lens, const int32_t *indices, const float *sinks,
+                        float scale, void *out, float *lse, void *workspace, void *stream)
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK) return st;
     if (!plan || !q || !k_pool || !block_table || !seq_lens || !out || !lse)
         return PA_ERR_INVALID;
+    if ((desc->topk > 0) != (indices != nullptr)) return PA_ERR_INVALID;
+    if (((uintptr_t)indices & 3) || ((uintptr_t)sinks & 3)) return PA_ERR_INVALID;
     const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
     const bool mla = desc->kv_format == PA_KV_MLA656;
     if (mla ? v_pool != nullptr : !v_pool) return PA_ERR_INVALID;
@@ -229,7 +234,11 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
                                                     desc->q_len * desc->Hkv * desc->G, desc->Dv))
                          : nullptr;
     a.seq_lens = seq_lens;
+    a.indices = indices;
+    a.sinks = sinks;
     a.q_len = desc->q_len;
+    a.window = desc->window;
+    a.topk = desc->topk;
     a.s_page_b = desc->s_page * eb;
     a.s_head_b = desc->s_head * eb;
     a.s_tok_b = desc->s_tok * eb;
@@ -257,14 +266,15 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
 }
 
 pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
-                            void *out, float *lse, void *stream)
+                            const float *sinks, void *out, float *lse, void *stream)
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK) return st;
     if (!plan || !out || !lse) return PA_ERR_INVALID;
     if (desc->num_splits == 1) return PA_OK;     // every request is a single chunk
     if (desc->flags & PA_FLAG_FUSED_COMBINE) return PA_OK;   // pa_decode_run merged
-    if (!workspace || !aligned16(workspace) || !aligned16(out) || ((uintptr_t)lse & 3))
+    if (!workspace || !aligned16(workspace) || !aligned16(out) || ((uintptr_t)lse & 3) ||
+        ((uintptr_t)sinks & 3))
         return PA_ERR_INVALID;
     PlanLayout L;
     st = layout_for(desc, &L);
@@ -274,7 +284,7 @@ pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const 
                                           pa::ws_o_bytes(L.max_items,
                                                          desc->q_len * desc->Hkv * desc->G,
                                                          desc->Dv));
-    if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, (uint16_t *)out, lse, desc->B,
+    if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, sinks, (uint16_t *)out, lse, desc->B,
                            desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
                            (hipStream_t)stream) != hipSuccess)
         return PA_ERR_DEVICE;

@@ -223,12 +223,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     qop[s] = bf16x8{};
             }
         }
-        // keys this column may see in the item: [t0, tlim) (the causal limit of its query
-        // token; every key of the item when q_len = 1)
-        int tlim = t1;
-        if (nq > 1) {
-            const int lim = seq_lens[b] - (nq - 1 - cqi);
-            tlim = lim < t1 ? lim : t1;
+        // keys this column may see in the item: [max(t0, tlo), tlim): the causal limit of
+        // its query token (every key of the item when q_len = 1) and the sliding window
+        int tlim = t1, tlo = 0;
+        if (nq > 1 || a.window > 0) {
+            const int L = seq_lens[b];
+            if (nq > 1) tlim = min(t1, L - (nq - 1 - cqi));
+            if (a.window > 0) tlo = max(0, L - nq + cqi - a.window + 1);
         }
 
         float m = -INFINITY;      // running max (log2 domain) of head `col`
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         for (int r = 0; r < 4; r++) {
                             const int tok = tb + 16 * sb + 4 * g4 + r;
                             const float x = st[sb][r] * f;
-                            sv[sb][r] = tok < tlim ? x : -INFINITY;
+                            sv[sb][r] = (tok < tlim && tok >= tlo) ? x : -INFINITY;
                             bm = fmaxf(bm, sv[sb][r]);
                         }
                     }
@@ -401,6 +402,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int w = 0; w < kWaves; w++) {
             const float mw = s_m[w][col];
             if (mw != -INFINITY) Lt += s_l[w][col] * fast_exp2(mw - M);
+        }
+        if (a.sinks && (flags & 1) && c < rows) {
+            // the item is the whole request: its sink joins the denominator here (split
+            // requests get it in the merge)
+            const float sk = a.sinks[h * G + cg] * 1.4426950408889634f;
+            const float M2 = fmaxf(M, sk);
+            if (M2 != -INFINITY) {
+                Lt = (M == -INFINITY ? 0.f : Lt * fast_exp2(M - M2)) + fast_exp2(sk - M2);
+                M = M2;
+            }
         }
         const float f = (m == -INFINITY || Lt == 0.f) ? 0.f : fast_exp2(m - M) / Lt;
         if (wave == 0 && lane < 16) {

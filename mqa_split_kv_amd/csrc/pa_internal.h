@@ -82,9 +82,13 @@ struct DecodeArgs {
     float *ws_lse;
     int64_t s_page_b, s_head_b, s_tok_b;   // pool strides in bytes
     const int32_t *seq_lens;    // [B]
+    const int32_t *indices;     // [B][topk] key positions (sparse) or null
+    const float *sinks;         // [Hq] sink logits (natural units) or null
     int B, Hkv, G, D, Dv, max_pages, page_shift;
     int q_len;                  // query tokens per request; query token i sees keys
                                 // [0, L - q_len + i + 1)
+    int window;                 // sliding window (0: off)
+    int topk;                   // sparse key slots per request (0: dense)
     int num_parts, part_begin_off, items_off, chunk_off_off;
     int32_t *counters;          // plan counter words; non-null: fused combine
     float scale_log2;           // logit scale * log2(e)
@@ -92,14 +96,14 @@ struct DecodeArgs {
 };
 
 hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout &L,
-                       int num_splits, hipStream_t stream);
+                       const pa_decode_desc *d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_append(const pa_decode_desc *d, int n_new, const void *k_new, const void *v_new,
                          const int32_t *block_table, const int32_t *seq_lens, void *k_pool,
                          void *v_pool, float *k_scale, float *v_scale, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
-                          uint16_t *out, float *lse, int B, int Hkv, int G, int q_len, int Dv,
-                          int chunk_off_off, hipStream_t stream);
+                          const float *sinks, uint16_t *out, float *lse, int B, int Hkv, int G,
+                          int q_len, int Dv, int chunk_off_off, hipStream_t stream);
 
 }  // namespace pa

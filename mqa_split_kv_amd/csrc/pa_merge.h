@@ -25,13 +25,16 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 // dependent load after another.  A unit's arithmetic does not depend on kUnits, so both
 // callers produce the same bits.  The result is
 //   out = sum_i exp(lse_i - M) O_i / sum_i exp(lse_i - M),  lse = M + ln sum_i exp(lse_i - M)
-// which is the merge equation above with exp(lse_i - lse) = exp(lse_i - M) / sum.
+// which is the merge equation above with exp(lse_i - lse) = exp(lse_i - M) / sum.  An
+// attention sink (sinks[hq], natural-log units, or null) joins once as one more partial
+// with lse = sink and O = 0 (XQA article, section "一个容易漏掉的细节: attention sink":
+// the final reduction adds the sink to the denominator).
 constexpr int kChunkBatch = 4;
 
 template <int kUnits>
-__device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16_t *out,
-                                  float *lse, int b, int64_t c0, int n, int Hq, int nq, int Dv,
-                                  int hq0, int nrows, int tid, int nthr)
+__device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const float *sinks,
+                                  uint16_t *out, float *lse, int b, int64_t c0, int n, int Hq,
+                                  int nq, int Dv, int hq0, int nrows, int tid, int nthr)
 {
     const int q4 = Dv / 4;
     const int total = nq * nrows * q4;
@@ -52,6 +55,10 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
             prow0[j] = c0 * Hr + qrow(ok[j] ? u : 0);
             m[j] = -INFINITY;
             s[j] = 0.f;
+            if (sinks && ok[j]) {
+                m[j] = sinks[hq0 + (u / q4) % nrows];   // the sink's partial: (sink, 1, 0)
+                s[j] = 1.f;
+            }
             acc[j] = merge_f32x4{0.f, 0.f, 0.f, 0.f};
         }
         for (int i0 = 0; i0 < n; i0 += kChunkBatch) {
@@ -116,7 +123,8 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, uint16
 // thread counts each of the workgroup's partial chunks in; the workgroup that counts a
 // request's last chunk acquires the other workgroups' writes, merges that request, and
 // returns its counter to zero.  Then requests with no chunk at all (length 0 under the
-// balanced rule) get out = 0, lse = -inf from workgroup part = b mod num_parts.
+// balanced rule) get out = 0, lse = -inf (or the sink) from workgroup part = b mod
+// num_parts.
 __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *plan, int part,
                                           int ib, int ie, int rg, int n_rowgroups, int hq0,
                                           int nrows, int arrivals, int *s_flag)
@@ -136,8 +144,8 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
         __syncthreads();
         if (*s_flag) {
             __threadfence();
-            merge_rows<4>(a.ws_o, a.ws_lse, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0, nrows,
-                          threadIdx.x, blockDim.x);
+            merge_rows<4>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
+                          nrows, threadIdx.x, blockDim.x);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
@@ -149,7 +157,7 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
             const int rr = u / q4, d0 = (u % q4) * 4;
             const int64_t row = ((int64_t)b * nq + rr / nrows) * Hq + hq0 + rr % nrows;
             *(merge_bf16x4 *)(a.out + row * a.Dv + d0) = merge_bf16x4{};
-            if (d0 == 0) a.lse[row] = -INFINITY;
+            if (d0 == 0) a.lse[row] = a.sinks ? a.sinks[hq0 + rr % nrows] : -INFINITY;
         }
     }
 }

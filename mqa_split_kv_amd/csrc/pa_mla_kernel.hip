@@ -30,6 +30,13 @@
 // The running max is only moved when a tile's max exceeds it by more than 2^8, so the
 // 128-register rescale is rare; probabilities stay below 2^8 and the result is the
 // same up to rounding (the reference cancels in the final normalisation).
+//
+// Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
+// indices): the items then cover index slots, and slot k of request b names the key
+// position indices[b][k].  Each wave loads its 8 tokens one per instruction, each
+// through a buffer resource over that token's 656 bytes (none for a slot outside the
+// request, which then reads as zeros), and records which of them are real in a per-tile
+// bit mask that the softmax applies.
 #include "pa_internal.h"
 
 namespace pa {
@@ -66,6 +73,11 @@ constexpr float kLazyMax = 8.0f;                   // log2 units
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <bool SPARSE>
+struct MlaCfg {
+    static constexpr int kDmaPerTile = SPARSE ? kTokPerWave : kDmaPerWave;   // per wave
+};
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -82,11 +94,15 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4 *)((PA_LDS uint8_t *)p));
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void pa_mla_kernel(
-    DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups)
+    DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups,
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ indices)
 {
+    constexpr int kDmaPerTile = MlaCfg<SPARSE>::kDmaPerTile;
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKTile];
+    __shared__ uint32_t s_valid[2];            // sparse: real-token bits of each K buffer
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -119,10 +135,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int t1 = plan[a.items_off + 4 * it + 2];
         const int flags = plan[a.items_off + 4 * it + 3];
         const int ntiles = (t1 - t0 + kT - 1) / kT;
+        // sliding window: the first key the query sees (one query token per request)
+        const int tlo = a.window > 0 ? max(0, seq_lens[b] - a.window) : 0;
+
+        // sparse: key position of index slot k (-1: outside the item or the request)
+        const int Lb = SPARSE ? seq_lens[b] : 0;
+        auto slot_pos = [&](int k) {
+            const int pos = k < t1 ? indices[(int64_t)b * a.topk + k] : -1;
+            return (pos >= 0 && pos < Lb) ? pos : -1;
+        };
 
         // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s (buffer
         //      loads over the 8 token rows: one 32-bit lane offset per instruction)
         auto dma_tile = [&](int j, int s) {
+            if (SPARSE) {
+                // one load per token, through a resource over that token's bytes only
+                const int jc = j < ntiles ? j : ntiles - 1;
+#pragma unroll
+                for (int tt = 0; tt < kTokPerWave; tt++) {
+                    const int pos = slot_pos(t0 + kT * jc + kTokPerWave * wave + tt);
+                    const int page = pos >= 0 ? bt[(int64_t)b * a.max_pages + (pos >> a.page_shift)] : 0;
+                    const int slot = pos >= 0 ? pos & ((1 << a.page_shift) - 1) : 0;
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot * a.s_tok_b),
+                        (short)0, pos >= 0 ? kTokBytes : 0, 0x00020000);
+                    uint8_t *dst = &raw[s][(kTokPerWave * wave + tt) * kTokBytes];
+                    if (lane < kChunks)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void *)dst, 16, 16 * lane, 0, 0, 0);
+                }
+                return;
+            }
             const int jc = j < ntiles ? j : ntiles - 1;     // past the end: reload the last tile
             int tw = t0 + kT * jc + kTokPerWave * wave;     // first of the wave's 8 tokens
             if (tw >= t1) tw = (t1 - 1) & ~(kTokPerWave - 1);
@@ -148,6 +190,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         auto dequant_tile = [&](int j, int s, int kb) {
             const int row0 = kTokPerWave * wave;
             const int tbase = t0 + kT * j + row0;
+            if (SPARSE) {
+                // bits of this wave's real tokens, byte `wave` of the tile's mask
+                uint32_t vm = 0;
+#pragma unroll
+                for (int tt = 0; tt < kTokPerWave; tt++) vm |= (slot_pos(tbase + tt) >= 0 ? 1u : 0u) << tt;
+                if (lane == 0) ((uint8_t *)&s_valid[kb])[wave] = (uint8_t)vm;
+            }
 #pragma unroll
             for (int tt = 0; tt < kTokPerWave; tt++) {
                 const uint8_t *tok = &raw[s][(row0 + tt) * kTokBytes];
@@ -194,7 +243,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (ntiles > 0) {
             dma_tile(0, 0);
             dma_tile(1, 1);
-            wait_vmcnt<kDmaPerWave>();            // own loads of tile 0 done
+            wait_vmcnt<kDmaPerTile>();            // own loads of tile 0 done
             dequant_tile(0, 0, 0);
             lds_barrier();
 
@@ -252,10 +301,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     // ---- online softmax with a lazily moved reference
                     float bm = -INFINITY;
                     float sv[8];
+                    const uint32_t vmask = SPARSE ? s_valid[j & 1] : 0u;
 #pragma unroll
                     for (int r = 0; r < 8; r++) {
-                        const int tok = t0 + kT * j + 16 * (r >> 2) + 4 * g4 + (r & 3);
-                        sv[r] = tok < t1 ? st[r >> 2][r & 3] * a.scale_log2 : -INFINITY;
+                        const int row = 16 * (r >> 2) + 4 * g4 + (r & 3);
+                        const int tok = t0 + kT * j + row;
+                        const bool vis = SPARSE ? ((vmask >> row) & 1u) != 0 : (tok < t1 && tok >= tlo);
+                        sv[r] = vis ? st[r >> 2][r & 3] * a.scale_log2 : -INFINITY;
                         bm = fmaxf(bm, sv[r]);
                     }
                     bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -300,7 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
                 // ---- next tile: own loads of tile j+1 done (tile j+2's are younger), then
                 //      dequantise it into the other K buffer
-                wait_vmcnt<kDmaPerWave>();
+                wait_vmcnt<kDmaPerTile>();
                 dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1);
                 lds_barrier();
             }
@@ -323,9 +375,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const int head = head0 + col;
-            const bool empty = m == -INFINITY || l == 0.f;
-            const float inv = empty ? 0.f : 1.0f / l;
-            const float lse_v = empty ? -INFINITY : (m + log2f(l)) * 0.69314718055994530942f;
+            float inv, lse_v;
+            const float sk = (a.sinks && (flags & 1)) ? a.sinks[head] * 1.4426950408889634f : -INFINITY;
+            const float M2 = fmaxf(m, sk);
+            if (M2 == -INFINITY || (sk == -INFINITY && l == 0.f)) {
+                inv = 0.f;                                   // nothing to attend to
+                lse_v = -INFINITY;
+            } else {
+                // a sink (whole-request items only; split requests get it in the merge)
+                // joins the denominator: den = l 2^(m - M2) + 2^(sk - M2)
+                const float fm = fast_exp2(m - M2);          // m = -inf: 0
+                const float den = l * fm + fast_exp2(sk - M2);
+                inv = fm / den;
+                lse_v = (M2 + log2f(den)) * 0.69314718055994530942f;
+            }
             const int64_t row = (int64_t)b * Hq + head;
             // O^T layout: lane holds dims 16db + 4g4 + e of head `col`
             if (flags & 1) {
@@ -356,8 +419,12 @@ hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream)
 {
     const int ngroups = (a.G + kHeadsPerWG - 1) / kHeadsPerWG;
     const int nwg = (a.num_parts + 7) / 8 * 8 * ngroups;
-    hipLaunchKernelGGL(pa_mla_kernel, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
-                       a.block_table, ngroups);
+    if (a.topk > 0)
+        hipLaunchKernelGGL(pa_mla_kernel<true>, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
+                           a.block_table, ngroups, a.seq_lens, a.indices);
+    else
+        hipLaunchKernelGGL(pa_mla_kernel<false>, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
+                           a.block_table, ngroups, a.seq_lens, a.indices);
     return hipGetLastError();
 }
 

@@ -8,6 +8,10 @@
 //    contiguous parts (FlashMLA walk-through, section 调度: work is shared out over
 //    the compute units ahead of the main kernel, equal per unit, and the result can
 //    be reused while shapes and lengths stay the same).
+// The tiles of request b cover keys [64 * first_b, len_b): len_b = L_b (topk index slots
+// for sparse decode) and first_b the tile of the earliest key a sliding window leaves
+// visible (XQA article, section "分页 KV: 页号怎么变成 TMA 坐标": leading pages outside
+// the window are never read), 0 otherwise.
 #include "pa_internal.h"
 
 namespace pa {
@@ -16,6 +20,19 @@ namespace {
 constexpr int kPlanThreads = 1024;
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+struct Span {
+    int q_len, window, topk;
+    // keys (or index slots) the request's items cover: [64 * first(L), len(L))
+    __device__ int len(int L) const { return topk > 0 ? topk : L; }
+    __device__ int first(int L) const
+    {
+        if (topk > 0 || window <= 0) return 0;
+        const int lo = L - q_len - window + 1;
+        return lo > 0 ? lo / kTileTokens : 0;
+    }
+    __device__ int tiles(int L) const { return ceil_div_i(len(L), kTileTokens) - first(L); }
+};
 
 // Exclusive scan of `n` ints in LDS (in place), returns the total.  All threads call.
 __device__ int block_exclusive_scan(int *v, int n, int *scratch)
@@ -49,7 +66,7 @@ __device__ int block_exclusive_scan(int *v, int n, int *scratch)
 __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
     const int32_t *__restrict__ seq_lens, int32_t *__restrict__ plan, int B, int num_parts,
     int max_items, int num_splits, int part_begin_off, int chunk_off_off, int items_off,
-    int counters_off, int n_counters)
+    int counters_off, int n_counters, Span sp)
 {
     __shared__ int s_start[kMaxBatch + 1];   // tile prefix S_b
     __shared__ int s_ne[kMaxBatch + 1];      // non-empty request prefix
@@ -67,11 +84,11 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
         const int n_items = B * s;
         for (int p = tid; p < n_items; p += kPlanThreads) {
             const int b = p / s, i = p % s;
-            const int L = seq_lens[b];
-            const int n = ceil_div_i(L, kTileTokens);
+            const int L = sp.len(seq_lens[b]), f = sp.first(seq_lens[b]);
+            const int n = sp.tiles(seq_lens[b]);
             const int per = ceil_div_i(n, s);
-            const int lo = i * per;
-            const int hi = min((i + 1) * per, n);
+            const int lo = f + i * per;
+            const int hi = f + min((i + 1) * per, n);
             const int t0 = min(lo * kTileTokens, L);
             int t1 = min(hi * kTileTokens, L);
             if (t1 < t0) t1 = t0;
@@ -91,7 +108,7 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
 
     // ---- balanced parts
     for (int b = tid; b < B; b += kPlanThreads) {
-        const int n = ceil_div_i(seq_lens[b], kTileTokens);
+        const int n = sp.tiles(seq_lens[b]);
         s_start[b] = n;
         s_ne[b] = n > 0 ? 1 : 0;
     }
@@ -200,8 +217,9 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
         for (int b = bf; b <= bl; b++) {
             const int S = s_start[b], n = s_start[b + 1] - S;
             if (n == 0) continue;
-            const int lo = max(e0, S) - S, hi = min(e1, S + n) - S;
-            const int L = seq_lens[b];
+            const int f = sp.first(seq_lens[b]);
+            const int lo = f + max(e0, S) - S, hi = f + min(e1, S + n) - S;
+            const int L = sp.len(seq_lens[b]);
             const int nch = chunk_off[b + 1] - chunk_off[b];
             items[4 * k + 0] = b;
             items[4 * k + 1] = lo * kTileTokens;
@@ -219,11 +237,15 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
 }  // namespace
 
 hipError_t launch_plan(const int32_t *seq_lens, int32_t *plan, const PlanLayout &L,
-                       int num_splits, hipStream_t stream)
+                       const pa_decode_desc *d, hipStream_t stream)
 {
+    Span sp;
+    sp.q_len = d->q_len;
+    sp.window = d->window;
+    sp.topk = d->topk;
     hipLaunchKernelGGL(pa_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, plan,
-                       L.B, L.num_parts, L.max_items, num_splits, L.part_begin_off,
-                       L.chunk_off_off, L.items_off, L.counters_off, L.n_counters);
+                       L.B, L.num_parts, L.max_items, d->num_splits, L.part_begin_off,
+                       L.chunk_off_off, L.items_off, L.counters_off, L.n_counters, sp);
     return hipGetLastError();
 }
 

@@ -18,6 +18,12 @@ partial result that the combine step merges.  Two partition rules:
   Every non-empty intersection of a part with a request is one item (chunk); items
   are numbered in (request, part) order, so a request's chunks are consecutive.
 
+Request spans: request b's tiles cover keys [T * first_b, len_b) with len_b = L_b
+(topk index slots for sparse decode) and first_b = floor(max(0, L_b - q_len - W + 1) / T)
+under a sliding window W (XQA article, section "分页 KV: 页号怎么变成 TMA 坐标": pages
+before the window are skipped), else 0.  The rules above apply to n_b = ceil(len_b / T)
+- first_b tiles, offset by first_b.
+
 Plan buffer (int32 words), shared contract with the library:
   [0] magic 0x50414450  [1] mode (0 fixed, 1 balanced)  [2] B  [3] num_parts
   [4] num_items  [5] T  [6] max_items  [7] 0
@@ -38,15 +44,25 @@ def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def fixed_items(seq_lens, num_splits: int, tile: int = TILE):
+def span(L: int, q_len: int = 1, window: int = 0, topk: int = 0, tile: int = TILE):
+    """(len, first tile) of a request of length L."""
+    if topk > 0:
+        return topk, 0
+    first = max(0, L - q_len - window + 1) // tile if window > 0 else 0
+    return L, first
+
+
+def fixed_items(seq_lens, num_splits: int, tile: int = TILE, q_len: int = 1, window: int = 0,
+                topk: int = 0):
     """Items (b, tok0, tok1) of the fixed-split rule, b-major, split-minor."""
     items = []
-    for b, L in enumerate(int(x) for x in seq_lens):
-        n = ceil_div(L, tile)
+    for b, L0 in enumerate(int(x) for x in seq_lens):
+        L, f = span(L0, q_len, window, topk, tile)
+        n = ceil_div(L, tile) - f
         per = ceil_div(n, num_splits)
         for i in range(num_splits):
-            lo = i * per
-            hi = min((i + 1) * per, n)
+            lo = f + i * per
+            hi = f + min((i + 1) * per, n)
             t0 = min(lo * tile, L)
             t1 = min(hi * tile, L)
             if t1 < t0:
@@ -55,14 +71,16 @@ def fixed_items(seq_lens, num_splits: int, tile: int = TILE):
     return items
 
 
-def balanced_items(seq_lens, num_parts: int, tile: int = TILE):
+def balanced_items(seq_lens, num_parts: int, tile: int = TILE, q_len: int = 1, window: int = 0,
+                   topk: int = 0):
     """Items (p, b, tok0, tok1) of the balanced rule, in (request, part) order."""
-    n = [ceil_div(int(L), tile) for L in seq_lens]
+    spans = [span(int(L), q_len, window, topk, tile) for L in seq_lens]
+    n = [ceil_div(L, tile) - f for (L, f) in spans]
     S = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
     N = int(S[-1])
     e = [(p * N) // num_parts for p in range(num_parts + 1)]
     items = []
-    for b, L in enumerate(int(x) for x in seq_lens):
+    for b, (L, f) in enumerate(spans):
         if n[b] == 0:
             continue
         for p in range(num_parts):
@@ -70,7 +88,7 @@ def balanced_items(seq_lens, num_parts: int, tile: int = TILE):
             hi = min(e[p + 1], int(S[b]) + n[b])
             if lo >= hi:
                 continue
-            lt0, lt1 = lo - int(S[b]), hi - int(S[b])
+            lt0, lt1 = f + lo - int(S[b]), f + hi - int(S[b])
             items.append((p, b, lt0 * tile, min(lt1 * tile, L)))
     return items
 
@@ -80,7 +98,7 @@ def max_items(B: int, num_splits: int, num_parts: int) -> int:
 
 
 def plan_words(seq_lens, num_splits: int, num_parts: int, tile: int = TILE,
-               n_rowgroups: int = 0) -> np.ndarray:
+               n_rowgroups: int = 0, q_len: int = 1, window: int = 0, topk: int = 0) -> np.ndarray:
     """The full plan buffer (int32) the plan kernel must write, for either rule.
 
     num_splits > 0 selects the fixed rule (num_parts is then B * num_splits);
@@ -89,12 +107,12 @@ def plan_words(seq_lens, num_splits: int, num_parts: int, tile: int = TILE,
     """
     B = len(seq_lens)
     if num_splits > 0:
-        its = fixed_items(seq_lens, num_splits, tile)
+        its = fixed_items(seq_lens, num_splits, tile, q_len, window, topk)
         P = B * num_splits
         flat = [(i, b, t0, t1) for i, (b, t0, t1) in enumerate(its)]
         mode = 0
     else:
-        flat = balanced_items(seq_lens, num_parts, tile)
+        flat = balanced_items(seq_lens, num_parts, tile, q_len, window, topk)
         P = num_parts
         mode = 1
     mi = max_items(B, num_splits, P)

@@ -25,7 +25,8 @@ def to_device(case: dict, device="cuda") -> dict:
     return dict(q=t(case["q"]), k_pool=t(case["k_pool"]),
                 v_pool=t(case["v_pool"]) if case.get("v_pool") is not None else None,
                 k_scale=t(case.get("k_scale")), v_scale=t(case.get("v_scale")),
-                block_table=t(case["block_table"]), seq_lens=t(case["seq_lens"]))
+                block_table=t(case["block_table"]), seq_lens=t(case["seq_lens"]),
+                indices=t(case.get("indices")), sinks=t(case.get("sinks")))
 
 
 def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
@@ -58,8 +59,8 @@ class GpuRun:
         d = self.dev
         self.runner.run(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                         self.out, self.lse, k_scale=d["k_scale"], v_scale=d["v_scale"],
-                        scale=scale)
-        self.runner.combine(self.out, self.lse)
+                        scale=scale, indices=d.get("indices"), sinks=d.get("sinks"))
+        self.runner.combine(self.out, self.lse, sinks=d.get("sinks"))
 
     def __call__(self, scale: float = 0.0):
         self.plan()

@@ -52,6 +52,11 @@ BAD = [
     (dict(s_tok=4), pb.PA_ERR_INVALID),          # 8-byte stride: not 16-byte aligned
     (dict(s_tok=56), pb.PA_ERR_INVALID),         # not a multiple of 16 bytes... 112 B
     (dict(num_splits=-1), pb.PA_ERR_INVALID),
+    (dict(window=-1), pb.PA_ERR_INVALID),
+    (dict(topk=-1), pb.PA_ERR_INVALID),
+    (dict(topk=64), pb.PA_ERR_UNSUPPORTED),      # sparse decode: MLA tokens only
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
+          topk=64, window=8), pb.PA_ERR_UNSUPPORTED),
     (dict(flags=2), pb.PA_ERR_INVALID),           # undefined flag bit
     (dict(flags=-1), pb.PA_ERR_INVALID),
     (dict(kv_format=7), pb.PA_ERR_INVALID),
@@ -107,34 +112,38 @@ def test_fused_flag_accepted_and_combine_is_launch_free():
     buf = ctypes.create_string_buffer(1 << 12)
     base = (ctypes.addressof(buf) + 255) // 256 * 256
     p = ctypes.c_void_p
-    assert pb.lib().pa_decode_combine(ctypes.byref(d), p(base), p(base), p(base), p(base),
+    assert pb.lib().pa_decode_combine(ctypes.byref(d), p(base), p(base), None, p(base), p(base),
                                       None) == pb.PA_OK
 
 
+def _run(d, base, **over):
+    """pa_decode_run with every pointer valid (host memory: only host-side checks run
+    before the first failing one) except the overrides."""
+    p = ctypes.c_void_p
+    a = dict(plan=p(base), q=p(base), k=p(base), v=p(base), ks=p(base), vs=p(base),
+             bt=p(base), sl=p(base), idx=None, sinks=None, scale=ctypes.c_float(0.0),
+             out=p(base), lse=p(base), ws=p(base))
+    a.update(over)
+    return pb.lib().pa_decode_run(ctypes.byref(d), a["plan"], a["q"], a["k"], a["v"], a["ks"],
+                                  a["vs"], a["bt"], a["sl"], a["idx"], a["sinks"], a["scale"],
+                                  a["out"], a["lse"], a["ws"], None)
+
+
 def test_run_rejects_null_and_misaligned_pointers():
-    L = pb.lib()
     d = _desc()
     buf = ctypes.create_string_buffer(1 << 16)
     base = (ctypes.addressof(buf) + 255) // 256 * 256
     p = ctypes.c_void_p
-    args_ok = [p(base)] * 9
-    # null plan
-    st = L.pa_decode_run(ctypes.byref(d), None, *[p(base)] * 7, ctypes.c_float(0.0), p(base),
-                         p(base), p(base), None)
-    assert st == pb.PA_ERR_INVALID
-    # misaligned q
-    st = L.pa_decode_run(ctypes.byref(d), p(base), p(base + 2), *[p(base)] * 6,
-                         ctypes.c_float(0.0), p(base), p(base), p(base), None)
-    assert st == pb.PA_ERR_INVALID
-    # non-finite scale
-    st = L.pa_decode_run(ctypes.byref(d), *args_ok[:8], ctypes.c_float(float("nan")), p(base),
-                         p(base), p(base), None)
-    assert st == pb.PA_ERR_INVALID
-    # fp8 without scale tables
+    assert _run(d, base, plan=None) == pb.PA_ERR_INVALID
+    assert _run(d, base, q=p(base + 2)) == pb.PA_ERR_INVALID
+    assert _run(d, base, scale=ctypes.c_float(float("nan"))) == pb.PA_ERR_INVALID
+    assert _run(d, base, sinks=p(base + 2)) == pb.PA_ERR_INVALID
+    assert _run(d, base, idx=p(base)) == pb.PA_ERR_INVALID            # indices without topk
     d8 = _desc(kv_format=pb.PA_KV_FP8_E4M3_PAGE_HEAD, s_tok=64, s_head=16 * 64, s_page=16 * 64)
-    st = L.pa_decode_run(ctypes.byref(d8), *[p(base)] * 4, None, None, p(base), p(base),
-                         ctypes.c_float(0.0), p(base), p(base), p(base), None)
-    assert st == pb.PA_ERR_INVALID
+    assert _run(d8, base, ks=None, vs=None) == pb.PA_ERR_INVALID
+    dm = _desc(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656,
+               s_page=656 * 16, topk=64)
+    assert _run(dm, base, v=None) == pb.PA_ERR_INVALID                # topk without indices
 
 
 def test_plan_size_check():
