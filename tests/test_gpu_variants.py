@@ -199,3 +199,28 @@ def test_sparse_plan_words(splits):
     got = plan_t.cpu().numpy()
     n = oplan.valid_words(ref)
     assert np.array_equal(got[:n], ref[:n])
+
+
+# ------------------------------------------------------------------------------ padding
+
+@pytest.mark.parametrize("which", ["mla", "mla_splits", "bf16", "fp8"])
+def test_nan_bytes_in_padding_slots_are_never_used(which):
+    """Slots past each request's last token in its last page hold all-ones bytes (NaN
+    codes, NaN scales, NaN bf16): the outputs stay finite and equal the oracle's."""
+    if which.startswith("mla"):
+        case = _mla_case((100, 33, 300, 64), G=64, P=64, splits=3 if which == "mla_splits" else 0)
+    elif which == "bf16":
+        case = _case(Hq=16, Hkv=2, D=128, P=64, lens=(100, 33, 300, 64))
+    else:
+        case = _case(fmt=synth.KV_FP8_PAGE_HEAD, Hq=16, Hkv=2, D=128, P=64, lens=(100, 33, 300, 64))
+    P = case["page_size"]
+    for b, L in enumerate(case["seq_lens"]):
+        if L % P == 0:
+            continue
+        page = case["block_table"][b, (L - 1) // P]
+        if which.startswith("mla"):
+            case["k_pool"][page, L % P:] = 0xFF
+        else:
+            for pool in (case["k_pool"], case["v_pool"]):
+                pool[page, :, L % P:] = 0xFFFF if pool.dtype == np.uint16 else 0xFF
+    _check(case)
