@@ -11,6 +11,12 @@ namespace {
 
 using pa::PlanLayout;
 
+// Decode workgroups per compute unit for the balanced plan (one 4-wave workgroup per
+// unit keeps enough KV loads in flight to stream at the HBM read ceiling).
+#ifndef PA_WGS_PER_CU
+#define PA_WGS_PER_CU 1
+#endif
+
 constexpr int kMaxDevices = 64;
 constexpr int kMaxQLen = 64;
 constexpr int kMaxAppendTokens = 65535;     // grid y of the MLA append
@@ -98,7 +104,7 @@ pa_status num_parts_for(const pa_decode_desc *d, int *np)
         const int ngroups = (d->G + 63) / 64;
         n = cu / ngroups;
     } else {
-        const int wgs_per_cu = 1;
+        const int wgs_per_cu = PA_WGS_PER_CU;
         n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
     }
     *np = n < 1 ? 1 : n;
