@@ -130,8 +130,14 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
                                           int nrows, int arrivals, int *s_flag)
 {
     const int Hq = a.Hkv * a.G, nq = a.q_len;
-    __threadfence();
-    __syncthreads();
+    // the release (a write-back of the XCD's L2) is only paid by workgroups that wrote
+    // partials: with every request in one chunk the fused path costs nothing
+    bool wrote = false;
+    for (int it = ib; it < ie; it++) wrote |= !(plan[a.items_off + 4 * it + 3] & 1);
+    if (wrote) {
+        __threadfence();
+        __syncthreads();
+    }
     for (int it = ib; it < ie; it++) {
         if (plan[a.items_off + 4 * it + 3] & 1) continue;   // single chunk: already final
         const int b = plan[a.items_off + 4 * it + 0];
