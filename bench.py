@@ -26,7 +26,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 MLA_FLOP_PER_TOKEN = 2 * 128 * (576 + 512)   # q.k over 576 dims and p.v over 512, 128 heads
 
 
-def counter_traffic(workload):
+def counter_traffic(workload, batch):
     """Calibrated HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE readings, or None when the kernel source has
     changed since they were taken (or none were taken for this workload)."""
@@ -34,7 +34,7 @@ def counter_traffic(workload):
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f)
-        w = rec["workloads"][workload]
+        w = rec["workloads"]["%s, B=%d" % (workload, batch)]
         with open(os.path.join(ROOT, w["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != w["source_sha256"]:
                 return None
@@ -180,7 +180,7 @@ def main():
     dec_gbs = kv_bytes / (decode_us * 1e-6) / 1e9
     fmt = {0: "bf16", 1: "fp8e4m3-kv/bf16", 2: "mla656-fp8/bf16"}[case["kv_format"]]
 
-    traffic = counter_traffic(case["name"])
+    traffic = counter_traffic(case["name"], B) if args.q_len == 1 else None
     if case["kv_format"] == 2:
         # MLA: 128 heads share each token, so the contraction is MFMA-bound
         tflops = MLA_FLOP_PER_TOKEN * float(np.sum(case["seq_lens"])) / (decode_us * 1e-6) / 1e12
