@@ -183,7 +183,8 @@ def main():
     traffic = counter_traffic(case["name"], B) if args.q_len == 1 else None
     if case["kv_format"] == 2:
         # MLA: 128 heads share each token, so the contraction is MFMA-bound
-        tflops = MLA_FLOP_PER_TOKEN * float(np.sum(case["seq_lens"])) / (decode_us * 1e-6) / 1e12
+        tflops = (MLA_FLOP_PER_TOKEN * args.q_len * float(np.sum(case["seq_lens"]))
+                  / (decode_us * 1e-6) / 1e12)
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "pa_mla_kernel"}

@@ -103,7 +103,9 @@ typedef struct {
        s_page = P*Hkv*D, s_head = D, s_tok = Hkv*D.  MLA: s_tok = 656, s_head unused.
        Every stride times the unit size must be a multiple of 16 bytes. */
     int64_t s_page, s_head, s_tok;
-    int32_t q_len;             /* query tokens per request: must be 1 */
+    int32_t q_len;             /* query tokens per request (a linear draft, token i sees keys
+                                  [0, L - q_len + i]): 1..64, G * q_len <= 256 for bf16/fp8,
+                                  <= 1024 for MLA */
     int32_t num_splits;        /* 0: balanced split scheduling; s > 0: s chunks per request */
     int32_t kv_format;         /* pa_kv_format */
     int32_t flags;             /* 0 or PA_FLAG_FUSED_COMBINE; other bits: PA_ERR_INVALID */

@@ -72,9 +72,9 @@ pa_status check_desc(const pa_decode_desc *d)
         // the MLA kernel keeps its whole register file for the tile loop; its chunks are
         // merged by the combine kernel only
         if (d->flags & PA_FLAG_FUSED_COMBINE) return PA_ERR_UNSUPPORTED;
-        if (d->q_len != 1) return PA_ERR_UNSUPPORTED;
         if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
         if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
+        if (d->G * d->q_len > 1024) return PA_ERR_UNSUPPORTED;         // 16 groups of 64 rows
         if (d->s_tok < 656) return PA_ERR_INVALID;
         return PA_OK;
     }
@@ -100,8 +100,8 @@ pa_status num_parts_for(const pa_decode_desc *d, int *np)
     if (cu <= 0) return PA_ERR_DEVICE;
     int n;
     if (d->kv_format == PA_KV_MLA656) {
-        // one workgroup per CU over all (part, 64-head group) pairs
-        const int ngroups = (d->G + 63) / 64;
+        // one workgroup per CU over all (part, 64-row group) pairs; rows = G x q_len
+        const int ngroups = (d->G * d->q_len + 63) / 64;
         n = cu / ngroups;
     } else {
         const int wgs_per_cu = PA_WGS_PER_CU;
@@ -116,7 +116,7 @@ pa_status layout_for(const pa_decode_desc *d, PlanLayout *L)
     int np = 0;
     pa_status st = num_parts_for(d, &np);
     if (st != PA_OK) return st;
-    const int rowgroups = d->kv_format == PA_KV_MLA656 ? (d->G + 63) / 64 : d->Hkv;
+    const int rowgroups = d->kv_format == PA_KV_MLA656 ? (d->G * d->q_len + 63) / 64 : d->Hkv;
     *L = pa::plan_layout(d->B, rowgroups, d->num_splits, np);
     return PA_OK;
 }

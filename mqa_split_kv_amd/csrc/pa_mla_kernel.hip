@@ -5,8 +5,10 @@
 // codes, 4 fp32 scales (one per 128 codes), 64 bf16 rope values.  The key is the 576
 // dequantised values, the value is their first 512 (V shares the latent with K).
 //
-// One workgroup (4 waves, one per SIMD) = one (part, group of 64 query heads); it walks
-// the part's items.  The two head groups of a part run as workgroups 8 ids apart, i.e.
+// One workgroup (4 waves, one per SIMD) = one (part, group of 64 query rows); it walks
+// the part's items.  Query rows are (draft token qi, head g) pairs, row qi * G + g, so with
+// several query tokens per request (a linear speculative draft) each wave's 16 rows share
+// one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a part run as workgroups 8 ids apart, i.e.
 // on the same XCD at about the same time, so the second read of each KV tile is an L2
 // hit (the FlashMLA walk-through shares one KV tile between two 64-head CTAs through a
 // cluster, section 计算环节一; here the L2 of the XCD plays that role).  Per 32-token tile:
@@ -94,7 +96,10 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4 *)((PA_LDS uint8_t *)p));
 }
 
-template <bool SPARSE>
+// SPARSE: index-slot items.  MASKED: a per-wave key range narrower than the item (draft
+// tokens' causal limits, a sliding window); a separate instantiation, because the plain
+// kernel sits at the register-file limit and any extra live value spills.
+template <bool SPARSE, bool MASKED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void pa_mla_kernel(
     DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ indices)
@@ -111,9 +116,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int part = (wg / (8 * ngroups)) * 8 + wg % 8;
     const int group = (wg / 8) % ngroups;
     if (part >= a.num_parts) return;               // padding of the last id block
-    const int G = a.G, Hq = a.Hkv * a.G;
-    const int head0 = group * kHeadsPerWG + wave * kHeadsPerWave;
-    const bool active = head0 < G;                 // wave-uniform
+    const int G = a.G, Hq = a.Hkv * a.G, nq = a.q_len;
+    const int row0 = group * kHeadsPerWG + wave * kHeadsPerWave;   // first query row
+    const bool active = row0 < G * nq;             // wave-uniform
+    const int qi = row0 / G;                       // the wave's draft token (G % 16 == 0)
+    const int head0 = row0 - qi * G;               // its first head
     const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
 
     // lane byte offset of chunk x = 64 i + lane (token x / 41, chunk x % 41) inside the
@@ -135,8 +142,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int t1 = plan[a.items_off + 4 * it + 2];
         const int flags = plan[a.items_off + 4 * it + 3];
         const int ntiles = (t1 - t0 + kT - 1) / kT;
-        // sliding window: the first key the query sees (one query token per request)
-        const int tlo = a.window > 0 ? max(0, seq_lens[b] - a.window) : 0;
+        // causal limit of the wave's draft token and the first key its window leaves
+        int tlim = t1, tlo = 0;
+        if (MASKED) {
+            const int L = seq_lens[b];
+            if (nq > 1) tlim = min(t1, L - (nq - 1 - qi));
+            if (a.window > 0) tlo = max(0, L - nq + qi - a.window + 1);
+        }
 
         // sparse: key position of index slot k (-1: outside the item or the request)
         const int Lb = SPARSE ? seq_lens[b] : 0;
@@ -229,7 +241,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // ---- Q^T operand of this wave's 32 heads (B of the 32x32x16 MFMA), resident
         bf16x8 qop[kKSteps];
         if (active) {
-            const uint16_t *qrow = a.q + ((int64_t)b * Hq + head0 + col) * kDqk;
+            const uint16_t *qrow = a.q + (((int64_t)b * nq + qi) * Hq + head0 + col) * kDqk;
 #pragma unroll
             for (int s = 0; s < kKSteps; s++) qop[s] = *(const bf16x8 *)(qrow + 32 * s + 8 * g4);
         }
@@ -306,7 +318,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                     for (int r = 0; r < 8; r++) {
                         const int row = 16 * (r >> 2) + 4 * g4 + (r & 3);
                         const int tok = t0 + kT * j + row;
-                        const bool vis = SPARSE ? ((vmask >> row) & 1u) != 0 : (tok < t1 && tok >= tlo);
+                        const bool vis = SPARSE ? ((vmask >> row) & 1u) != 0
+                                                : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
                         sv[r] = vis ? st[r >> 2][r & 3] * a.scale_log2 : -INFINITY;
                         bm = fmaxf(bm, sv[r]);
                     }
@@ -389,7 +402,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 inv = fm / den;
                 lse_v = (M2 + log2f(den)) * 0.69314718055994530942f;
             }
-            const int64_t row = (int64_t)b * Hq + head;
+            const int64_t qr = (int64_t)qi * Hq + head;      // query row within the request
+            const int64_t row = (int64_t)b * nq * Hq + qr;
             // O^T layout: lane holds dims 16db + 4g4 + e of head `col`
             if (flags & 1) {
                 uint16_t *orow = a.out + row * kDv + 4 * g4;
@@ -402,7 +416,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 }
                 if (g4 == 0) a.lse[row] = lse_v;
             } else {
-                const int64_t prow = (int64_t)it * Hq + head;
+                const int64_t prow = (int64_t)it * nq * Hq + qr;
                 float *orow = a.ws_o + prow * kDv + 4 * g4;
 #pragma unroll
                 for (int db = 0; db < kDvBlocks; db++) *(f32x4 *)(orow + 16 * db) = acc[db] * inv;
@@ -417,14 +431,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 hipError_t launch_mla(const DecodeArgs &a, hipStream_t stream)
 {
-    const int ngroups = (a.G + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int ngroups = (a.G * a.q_len + kHeadsPerWG - 1) / kHeadsPerWG;
     const int nwg = (a.num_parts + 7) / 8 * 8 * ngroups;
     if (a.topk > 0)
-        hipLaunchKernelGGL(pa_mla_kernel<true>, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
-                           a.block_table, ngroups, a.seq_lens, a.indices);
+        hipLaunchKernelGGL((pa_mla_kernel<true, false>), dim3(nwg), dim3(kThreads), 0, stream, a,
+                           a.plan, a.block_table, ngroups, a.seq_lens, a.indices);
+    else if (a.q_len > 1 || a.window > 0)
+        hipLaunchKernelGGL((pa_mla_kernel<false, true>), dim3(nwg), dim3(kThreads), 0, stream, a,
+                           a.plan, a.block_table, ngroups, a.seq_lens, a.indices);
     else
-        hipLaunchKernelGGL(pa_mla_kernel<false>, dim3(nwg), dim3(kThreads), 0, stream, a, a.plan,
-                           a.block_table, ngroups, a.seq_lens, a.indices);
+        hipLaunchKernelGGL((pa_mla_kernel<false, false>), dim3(nwg), dim3(kThreads), 0, stream, a,
+                           a.plan, a.block_table, ngroups, a.seq_lens, a.indices);
     return hipGetLastError();
 }
 

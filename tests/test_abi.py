@@ -68,8 +68,8 @@ BAD = [
     (dict(q_len=0), pb.PA_ERR_INVALID),
     (dict(q_len=65), pb.PA_ERR_UNSUPPORTED),
     (dict(G=8, q_len=33), pb.PA_ERR_UNSUPPORTED),   # more than 256 query rows per KV head
-    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
-          q_len=2), pb.PA_ERR_UNSUPPORTED),
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=128, D=576, Dv=512, s_tok=656, s_page=656 * 16,
+          q_len=9), pb.PA_ERR_UNSUPPORTED),     # more than 1024 query rows
     (dict(B=5000), pb.PA_ERR_UNSUPPORTED),
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
      pb.PA_ERR_UNSUPPORTED),

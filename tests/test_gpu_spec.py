@@ -90,3 +90,33 @@ def test_spec_llama70b_shape_sampled():
     ref_out, ref_lse = oracle.decode(case, pairs=pairs)
     rows = np.repeat(pairs, G, axis=1)[:, None, :].repeat(2, axis=1)
     assert_parity(case, out, lse, ref_out, ref_lse, rows=rows)
+
+
+def _mla_spec(q_len, lens, G=64, P=64, splits=0, seed=41):
+    used = sum(-(-L // P) for L in lens)
+    spec = synth.CaseSpec(B=len(lens), Hq=G, Hkv=1, D=576, Dv=512, page_size=P, seq_lens=lens,
+                          kv_format=synth.KV_MLA656, pool_pages=used + 2, num_splits=splits,
+                          q_len=q_len)
+    return synth.make_case(spec, seed)
+
+
+@pytest.mark.parametrize("kw", [dict(q_len=2, lens=(300, 2, 1000)),
+                                dict(q_len=2, lens=(300, 2, 1000), G=128, splits=3),
+                                dict(q_len=3, lens=(65, 700), G=16, P=32, splits=1),
+                                dict(q_len=4, lens=(5000, 3), G=32)])
+def test_spec_mla_parity(kw):
+    case = _mla_spec(**kw)
+    out, lse = GpuRun(case)()
+    ref_out, ref_lse = oracle.decode(case)
+    assert out.shape == ref_out.shape
+    assert_parity(case, out, lse, ref_out, ref_lse)
+
+
+def test_spec_mla_with_window_and_sinks():
+    case = _mla_spec(2, (700, 40, 1300), G=64)
+    rng = np.random.default_rng(12)
+    case["window"] = 200
+    case["sinks"] = (rng.standard_normal(64) + 1.0).astype(np.float32)
+    out, lse = GpuRun(case)()
+    ref_out, ref_lse = oracle.decode(case)
+    assert_parity(case, out, lse, ref_out, ref_lse)
