@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="batch of the HD64 workload (1 or 8)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per request (linear speculative draft)")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="sparse decode over topk listed positions per request (MLA workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
@@ -81,6 +83,8 @@ def main():
     t_gen = time.time()
     case = synth.config_case(args.config, B=args.batch, **({"q_len": args.q_len}
                                                            if args.q_len != 1 else {}))
+    if args.topk:
+        case.update(topk=args.topk, indices=synth.sparse_indices(case, args.topk, 7000 + args.config))
     gen_s = time.time() - t_gen
     print(f"[bench] generated workload {args.config} ({case['name']}) in {gen_s:.1f}s", file=sys.stderr,
           flush=True)
@@ -96,6 +100,7 @@ def main():
     ks = dev(case["k_scale"]) if case.get("k_scale") is not None else None
     vs = dev(case["v_scale"]) if case.get("v_scale") is not None else None
     bt, sl = dev(case["block_table"]), dev(case["seq_lens"])
+    idx = dev(case["indices"]) if args.topk else None
     B, Hq, Dv = case["B"], case["Hkv"] * case["G"], case["Dv"]
     out = torch.empty((B, args.q_len, Hq, Dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, args.q_len, Hq), dtype=torch.float32, device="cuda")
@@ -115,7 +120,7 @@ def main():
     plan_us = e0.elapsed_time(e1) * 1000.0 / 10
 
     def step():
-        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs)
+        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs, indices=idx)
         runner.combine(out, lse)
 
     for _ in range(args.warmup):
@@ -139,7 +144,7 @@ def main():
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for _ in range(nk):
-        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs)
+        runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs, indices=idx)
     k1.record(stream)
     torch.cuda.synchronize()
     decode_us = k0.elapsed_time(k1) * 1000.0 / nk
@@ -180,11 +185,11 @@ def main():
     dec_gbs = kv_bytes / (decode_us * 1e-6) / 1e9
     fmt = {0: "bf16", 1: "fp8e4m3-kv/bf16", 2: "mla656-fp8/bf16"}[case["kv_format"]]
 
-    traffic = counter_traffic(case["name"], B) if args.q_len == 1 else None
+    traffic = counter_traffic(case["name"], B) if args.q_len == 1 and not args.topk else None
     if case["kv_format"] == 2:
         # MLA: 128 heads share each token, so the contraction is MFMA-bound
-        tflops = (MLA_FLOP_PER_TOKEN * args.q_len * float(np.sum(case["seq_lens"]))
-                  / (decode_us * 1e-6) / 1e12)
+        tokens = kv_bytes / synth.MLA_TOKEN_BYTES      # attended keys (listed ones if sparse)
+        tflops = MLA_FLOP_PER_TOKEN * args.q_len * tokens / (decode_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "pa_mla_kernel"}
@@ -200,7 +205,7 @@ def main():
 
     cfg = {"workload": case["name"], "B": B, "Hq": Hq, "Hkv": case["Hkv"], "D": case["D"],
            "Dv": Dv, "page_size": case["page_size"], "seq_len_total": int(np.sum(case["seq_lens"])),
-           "kv_format": fmt, "q_len": args.q_len, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
+           "kv_format": fmt, "q_len": args.q_len, "topk": args.topk or None, "num_splits": "balanced plan" if desc.num_splits == 0 else desc.num_splits,
            "num_parts": pb.pa_decode_num_parts(desc),
            "combine": "fused in the decode kernel" if args.fused_combine else "combine kernel",
            "parallelism": "single GPU"}
@@ -242,6 +247,9 @@ def cpu_baseline(case, seconds):
     B, Hkv = case["B"], case["Hkv"]
     threads = oracle.threads(0)
     L = np.asarray(case["seq_lens"], np.int64)
+    if case.get("topk"):                            # keys each request attends to
+        idx = np.asarray(case["indices"])
+        L = ((idx >= 0) & (idx < L[:, None])).sum(axis=1).astype(np.int64)
     order = [(b, h) for b in range(B) for h in range(Hkv)]
     n = max(1, min(len(order), threads))
     spent, done_pairs, done_tokens, reps = 0.0, 0, 0, 1

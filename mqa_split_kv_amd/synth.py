@@ -212,9 +212,26 @@ def config_case(index: int, B: Optional[int] = None, seed: Optional[int] = None,
     return make_case(spec, SEED_BASE + index if seed is None else seed)
 
 
+def sparse_indices(case: dict, topk: int, seed: int) -> np.ndarray:
+    """[B, topk] int32 key positions for sparse decode: distinct positions drawn uniformly
+    from each request's [0, L), ascending (a request shorter than topk lists all of its
+    positions, then -1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.full((case["B"], topk), -1, np.int32)
+    for b, L in enumerate(int(x) for x in case["seq_lens"]):
+        n = min(L, topk)
+        out[b, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    return out
+
+
 def kv_bytes(case: dict) -> int:
     """Algorithmic KV bytes of one decode step: every valid token's K and V read once
-    per KV head (fp8: plus one K and one V scale per (page, head) touched)."""
+    per KV head (fp8: plus one K and one V scale per (page, head) touched); for sparse
+    decode, every listed valid position once."""
+    if case.get("topk"):
+        idx = np.asarray(case["indices"])
+        L = np.asarray(case["seq_lens"], np.int64)[:, None]
+        return int(((idx >= 0) & (idx < L)).sum() * MLA_TOKEN_BYTES)
     L = np.asarray(case["seq_lens"], np.int64)
     Hkv, D, Dv, P = case["Hkv"], case["D"], case["Dv"], case["page_size"]
     fmt = case["kv_format"]
