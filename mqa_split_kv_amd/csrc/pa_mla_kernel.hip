@@ -35,10 +35,15 @@
 //
 // Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
 // indices): the items then cover index slots, and slot k of request b names the key
-// position indices[b][k].  Each wave loads its 8 tokens one per instruction, each
-// through a buffer resource over that token's 656 bytes (none for a slot outside the
-// request, which then reads as zeros), and records which of them are real in a per-tile
-// bit mask that the softmax applies.
+// position indices[b][k].  The address of a listed token takes two dependent lookups
+// (index, then block table), so they run ahead of the KV loads as per-lane vector loads
+// (lanes 0-7: the wave's 8 tokens): tile j+4's indices and tile j+3's page ids are loaded
+// while tile j is computed, and tile j+2's 8 tokens are gathered by direct-to-LDS loads
+// with per-lane 64-bit addresses (41 chunks per token, 6 instructions per wave).  All of
+// them go through the same in-order load counter as the KV tile, so the wait for tile
+// j+1 also completes the lookups.  A slot outside the item or the request loads a dummy
+// token that the conversion zeroes, and a per-tile bit mask of the real tokens is
+// applied in the softmax.
 #include "pa_internal.h"
 
 namespace pa {
@@ -77,7 +82,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <bool SPARSE>
 struct MlaCfg {
-    static constexpr int kDmaPerTile = SPARSE ? kTokPerWave : kDmaPerWave;   // per wave
+    // loads per wave and tile (sparse: the KV gather plus one index and one page-id load)
+    static constexpr int kDmaPerTile = SPARSE ? kDmaPerWave + 2 : kDmaPerWave;
 };
 
 template <int N>
@@ -90,6 +96,12 @@ __device__ __forceinline__ void wait_vmcnt()
 // Barrier for LDS handoffs only: this wave's LDS writes are complete, then all waves
 // meet.  (A full __syncthreads would also drain the in-flight KV loads.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// byte address of a shared-memory location, as LDS instructions take it
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(PA_LDS const void *)p;
+}
 
 __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p)
 {
@@ -108,6 +120,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKTile];
     __shared__ uint32_t s_valid[2];            // sparse: real-token bits of each K buffer
+    // sparse lookups: [position | page id][tile % 4][wave][token]
+    __shared__ int32_t s_look[SPARSE ? 2 * 4 * kWaves * kTokPerWave : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -124,13 +138,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
 
     // lane byte offset of chunk x = 64 i + lane (token x / 41, chunk x % 41) inside the
-    // 8 token rows a wave loads per tile
+    // 8 token rows a wave loads per tile (the sparse gather recomputes its split)
     int dma_off[kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; i++) {
         const int x = 64 * i + lane;
         const int tt = x / kChunks, c = x - tt * kChunks;
-        dma_off[i] = tt * (int)a.s_tok_b + 16 * c;
+        dma_off[i] = SPARSE ? 0 : tt * (int)a.s_tok_b + 16 * c;
     }
 
     const int ib = plan[a.part_begin_off + part];
@@ -150,33 +164,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (a.window > 0) tlo = max(0, L - nq + qi - a.window + 1);
         }
 
-        // sparse: key position of index slot k (-1: outside the item or the request)
+        // sparse lookups, lane l: token l % 8 of the wave's 8 in tile j, index slot k.  They
+        // go to shared memory by direct-to-LDS loads (no registers live across the tile
+        // compute; the loads complete in order with the KV gathers) and are read back by
+        // inline asm (which the compiler does not make wait for the gathers in flight).
         const int Lb = SPARSE ? seq_lens[b] : 0;
-        auto slot_pos = [&](int k) {
-            const int pos = k < t1 ? indices[(int64_t)b * a.topk + k] : -1;
-            return (pos >= 0 && pos < Lb) ? pos : -1;
+        auto sp_slot = [&](int j) { return t0 + kT * j + kTokPerWave * wave + (lane & 7); };
+        auto sp_ok = [&](int j, int pos) { return sp_slot(j) < t1 && pos >= 0 && pos < Lb; };
+        auto look = [&](int which, int j) { return &s_look[((which * 4 + (j & 3)) * kWaves + wave) * kTokPerWave]; };
+        auto sp_issue_pos = [&](int j) {           // slots past the row: its last entry
+            if (lane < kTokPerWave)
+                __builtin_amdgcn_global_load_lds((const void *)(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1)),
+                                                 (PA_LDS void *)look(0, j), 4, 0, 0);
+        };
+        auto sp_issue_page = [&](int j, int pos) { // no real token: the row's first page
+            if (lane < kTokPerWave)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(bt + (int64_t)b * a.max_pages + (sp_ok(j, pos) ? pos >> a.page_shift : 0)),
+                    (PA_LDS void *)look(1, j), 4, 0, 0);
+        };
+        auto sp_read = [&](int which, int j) {     // issue only: complete after lgkm_wait
+            int v;
+            asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(lds_addr(look(which, j)) + 4 * (lane & 7)));
+            return v;
+        };
+        auto lgkm_wait = [](int &x, int &y, int &z) {
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z)::"memory");
         };
 
         // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s (buffer
         //      loads over the 8 token rows: one 32-bit lane offset per instruction)
-        auto dma_tile = [&](int j, int s) {
-            if (SPARSE) {
-                // one load per token, through a resource over that token's bytes only
-                const int jc = j < ntiles ? j : ntiles - 1;
+        // sparse: gather of the wave's 8 listed tokens of tile j (position pos and page id
+        // page in lane l % 8) into raw slot s; returns the bits of the real tokens.  A
+        // token that is not real loads the first token of page 0 instead.
+        auto dma_sparse = [&](int j, int s, int pos, int page) {
+            const bool ok = sp_ok(j, pos);
+            const int64_t off = ok ? (int64_t)page * a.s_page_b +
+                                         (int64_t)(pos & ((1 << a.page_shift) - 1)) * a.s_tok_b
+                                   : 0;
+            const int lo = (int)(uint32_t)off, hi = (int)(off >> 32);
+            uint8_t *dst = &raw[s][wave * kWaveChunks * 16];
 #pragma unroll
-                for (int tt = 0; tt < kTokPerWave; tt++) {
-                    const int pos = slot_pos(t0 + kT * jc + kTokPerWave * wave + tt);
-                    const int page = pos >= 0 ? bt[(int64_t)b * a.max_pages + (pos >> a.page_shift)] : 0;
-                    const int slot = pos >= 0 ? pos & ((1 << a.page_shift) - 1) : 0;
-                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                        (void *)(a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot * a.s_tok_b),
-                        (short)0, pos >= 0 ? kTokBytes : 0, 0x00020000);
-                    uint8_t *dst = &raw[s][(kTokPerWave * wave + tt) * kTokBytes];
-                    if (lane < kChunks)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void *)dst, 16, 16 * lane, 0, 0, 0);
-                }
-                return;
+            for (int i = 0; i < kDmaPerWave; i++) {
+                // chunk x = 64 i + lane: token x / 41 (as x * 1599 >> 16, exact for x < 1681)
+                const int x = 64 * i + lane;
+                const int tt = (x * 1599) >> 16, c = x - kChunks * tt;
+                const uint32_t tlo = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * tt, lo);
+                const uint32_t thi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * tt, hi);
+                const uint8_t *g = a.k_pool + (int64_t)(((uint64_t)thi << 32) | tlo) + 16 * c;
+                if (64 * i + lane < kWaveChunks)
+                    __builtin_amdgcn_global_load_lds((const void *)g, (PA_LDS void *)(dst + 64 * 16 * i), 16,
+                                                     0, 0);
             }
+            return (uint32_t)__ballot(ok) & 0xFFu;
+        };
+
+        auto dma_tile = [&](int j, int s) {
             const int jc = j < ntiles ? j : ntiles - 1;     // past the end: reload the last tile
             int tw = t0 + kT * jc + kTokPerWave * wave;     // first of the wave's 8 tokens
             if (tw >= t1) tw = (t1 - 1) & ~(kTokPerWave - 1);
@@ -199,41 +242,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         //      writes: 16 neighbouring lanes touch 256 contiguous bytes, no bank conflicts);
         //      then the rope chunks (lane: token l / 8, chunk l % 8) and the 4 tile scales
         //      (lanes 0-7, into the row padding).  Rows of tokens >= t1 become 0.
-        auto dequant_tile = [&](int j, int s, int kb) {
+        //      Sparse: vm holds the bits of the wave's real tokens (byte `wave` of the
+        //      tile's mask); the other rows become 0.
+        auto dequant_tile = [&](int j, int s, int kb, uint32_t vm) {
             const int row0 = kTokPerWave * wave;
             const int tbase = t0 + kT * j + row0;
-            if (SPARSE) {
-                // bits of this wave's real tokens, byte `wave` of the tile's mask
-                uint32_t vm = 0;
+            auto dead = [&](int tt) { return SPARSE ? ((vm >> tt) & 1u) == 0 : tbase + tt >= t1; };
+            if (SPARSE && lane == 0) ((uint8_t *)&s_valid[kb])[wave] = (uint8_t)vm;
+            // the raw slot is read by inline asm: the compiler cannot tell these reads from
+            // the direct-to-LDS writes of later tiles still in flight, and before plain
+            // reads it would wait for those too (all loads of this wave), emptying the ring
+            const uint32_t rbase = lds_addr(&raw[s][row0 * kTokBytes]);
+            uint64_t w[kTokPerWave];
+            u32x4 rope, scl;
 #pragma unroll
-                for (int tt = 0; tt < kTokPerWave; tt++) vm |= (slot_pos(tbase + tt) >= 0 ? 1u : 0u) << tt;
-                if (lane == 0) ((uint8_t *)&s_valid[kb])[wave] = (uint8_t)vm;
-            }
+            for (int tt = 0; tt < kTokPerWave; tt++)
+                asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(w[tt]) : "v"(rbase + 8 * lane), "n"(tt * kTokBytes));
+            asm volatile("ds_read_b128 %0, %1 offset:528" : "=v"(rope)
+                         : "v"(rbase + (lane >> 3) * kTokBytes + 16 * (lane & 7)));
+            asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(scl) : "v"(rbase + (lane & 7) * kTokBytes));
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
+                           "+v"(w[6]), "+v"(w[7]), "+v"(rope), "+v"(scl)::"memory");
 #pragma unroll
             for (int tt = 0; tt < kTokPerWave; tt++) {
-                const uint8_t *tok = &raw[s][(row0 + tt) * kTokBytes];
-                const uint2 w = *(const uint2 *)(tok + 8 * lane);
+                const int lo = (int)(uint32_t)w[tt], hi = (int)(w[tt] >> 32);
                 bf16x8 o;
-                const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
-                const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
-                const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
-                const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+                const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+                const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+                const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+                const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
                 o[0] = b0[0]; o[1] = b0[1]; o[2] = b1[0]; o[3] = b1[1];
                 o[4] = b2[0]; o[5] = b2[1]; o[6] = b3[0]; o[7] = b3[1];
-                if (tbase + tt >= t1) o = bf16x8{};
+                if (dead(tt)) o = bf16x8{};
                 *(bf16x8 *)(&ktile[kb][(row0 + tt) * kKRow + 16 * lane]) = o;
             }
             {
                 const int tt = lane >> 3, c = lane & 7;
-                const uint8_t *tok = &raw[s][(row0 + tt) * kTokBytes];
-                u32x4 rope = *(const u32x4 *)(tok + 528 + 16 * c);
-                if (tbase + tt >= t1) rope = u32x4{0, 0, 0, 0};
+                if (dead(tt)) rope = u32x4{0, 0, 0, 0};
                 *(u32x4 *)(&ktile[kb][(row0 + tt) * kKRow + (512 + 8 * c) * 2]) = rope;
             }
             if (lane < kTokPerWave) {
-                const uint8_t *tok = &raw[s][(row0 + lane) * kTokBytes];
-                u32x4 scl = *(const u32x4 *)(tok + 512);
-                if (tbase + lane >= t1) scl = u32x4{0, 0, 0, 0};
+                if (dead(lane)) scl = u32x4{0, 0, 0, 0};
                 *(u32x4 *)(&ktile[kb][(row0 + lane) * kKRow + kDqk * 2]) = scl;
             }
         };
@@ -253,10 +303,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         float l = 0.f;
 
         if (ntiles > 0) {
-            dma_tile(0, 0);
-            dma_tile(1, 1);
-            wait_vmcnt<kDmaPerTile>();            // own loads of tile 0 done
-            dequant_tile(0, 0, 0);
+            // sparse pipeline at the top of tile j: the positions of tiles j+2 and j+3 and
+            // the page ids of tile j+2 are in shared memory, vm1 = real-token bits of j+1
+            uint32_t vm0 = 0, vm1 = 0, vm2 = 0;
+            if (SPARSE) {
+                // positions of tiles 0-3, page ids of tiles 0-2, gathers of tiles 0 and 1
+                for (int t = 0; t < 4; t++) sp_issue_pos(t);
+                wait_vmcnt<0>();
+                int p0 = sp_read(0, 0), p1 = sp_read(0, 1), p2 = sp_read(0, 2);
+                lgkm_wait(p0, p1, p2);
+                sp_issue_page(0, p0);
+                sp_issue_page(1, p1);
+                sp_issue_page(2, p2);
+                wait_vmcnt<0>();
+                int g0 = sp_read(1, 0), g1 = sp_read(1, 1), unused = 0;
+                lgkm_wait(g0, g1, unused);
+                vm0 = dma_sparse(0, 0, p0, g0);
+                vm1 = dma_sparse(1, 1, p1, g1);
+                wait_vmcnt<kDmaPerWave>();        // tile 0 done (tile 1's gather is younger)
+            } else {
+                dma_tile(0, 0);
+                dma_tile(1, 1);
+                wait_vmcnt<kDmaPerTile>();        // own loads of tile 0 done
+            }
+            dequant_tile(0, 0, 0, vm0);
             lds_barrier();
 
             // The tile loop never rescales O^T itself: when a tile's max exceeds the
@@ -271,7 +341,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 // tile j+2's loads go out before the compute of tile j (once per tile, also
                 // when the loop resumes at j after a rescale)
                 if (dma_next == j + 2) {
-                    dma_tile(j + 2, (j + 2) % kRawSlots);
+                    if (SPARSE) {
+                        // the previous tile's lookups are done (tile j+1's gather is
+                        // younger); issue tile j+3's page ids and tile j+4's positions
+                        // (the next tile waits for these, not for this tile's KV), then
+                        // the gather of tile j+2
+                        wait_vmcnt<kDmaPerWave>();
+                        int p3 = sp_read(0, j + 3), p2 = sp_read(0, j + 2), g2 = sp_read(1, j + 2);
+                        lgkm_wait(p3, p2, g2);
+                        sp_issue_page(j + 3, p3);
+                        sp_issue_pos(j + 4);
+                        vm2 = dma_sparse(j + 2, (j + 2) % kRawSlots, p2, g2);
+                    } else {
+                        dma_tile(j + 2, (j + 2) % kRawSlots);
+                    }
                     dma_next++;
                 }
                 const uint8_t *kt = ktile[j & 1];
@@ -366,7 +449,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 // ---- next tile: own loads of tile j+1 done (tile j+2's are younger), then
                 //      dequantise it into the other K buffer
                 wait_vmcnt<kDmaPerTile>();
-                dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1);
+                dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1, vm1);
+                vm1 = vm2;
                 lds_barrier();
             }
             if (j >= ntiles) break;
