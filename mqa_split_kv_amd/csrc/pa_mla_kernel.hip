@@ -8,27 +8,42 @@
 // One workgroup (4 waves, one per SIMD) = one (part, group of 64 query rows); it walks
 // the part's items.  Query rows are (draft token qi, head g) pairs, row qi * G + g, so with
 // several query tokens per request (a linear speculative draft) each wave's 16 rows share
-// one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a part run as workgroups 8 ids apart, i.e.
-// on the same XCD at about the same time, so the second read of each KV tile is an L2
-// hit (the FlashMLA walk-through shares one KV tile between two 64-head CTAs through a
-// cluster, section 计算环节一; here the L2 of the XCD plays that role).  Per 32-token tile:
-//   * raw tile: the 32 tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads into a
-//     3-slot ring (two tiles in flight while one is computed); each wave loads and
-//     later dequantises 8 of the tokens, so it only ever waits for its own loads;
-//   * conversion once per tile (not per head): e4m3 -> bf16 is exact, so the codes go
-//     to a double-buffered bf16 K tile in LDS unscaled, with the token's 4 fp32 tile
-//     scales in the row padding, and the rope values copied (FlashMLA walk-through:
-//     dequantise to bf16 and run bf16 MMA with fp32 accumulation; section 计算环节一
-//     for why dequantisation is the hot spot).  The scales are applied in fp32 instead
-//     of being rounded into the bf16 values: S = sum_t scale_t (q_t . k_t) + q_rope .
-//     k_rope over the four 128-dim tiles t, and for the value dims of tile t the
-//     probabilities are multiplied by scale_t before the PV product;
-//   * each wave owns 16 query heads: S^T[16 tok x 16 heads] = K . Q^T with bf16 MFMA
-//     16x16x32 (K from the LDS tile, Q^T resident in 72 registers), an online softmax
-//     per head column, and O^T[512 x 16 heads] += V^T . P^T with the V^T operand read
-//     back transposed (ds_read_b64_tr_b16) from the same tile; O^T lives in 128
-//     accumulation registers (the register-budget problem the FlashMLA walk-through
-//     describes in section 计算环节二).
+// one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a part
+// run as workgroups 8 ids apart, i.e. on the same XCD at about the same time, so the
+// second read of each KV tile is an L2 hit (the FlashMLA walk-through shares one KV tile
+// between two 64-head CTAs through a cluster, section 计算环节一; here the L2 of the XCD
+// plays that role).
+//
+// Per 32-token tile:
+//   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
+//     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 6-slot
+//     ring of 672-byte rows, so each tile's loads are issued 5 tiles ahead;
+//   * the FP8 codes stay FP8 in LDS: each wave converts the MFMA operands it reads to
+//     bf16 in registers right before the MFMA (e4m3 -> bf16 is exact).  A bf16 copy of
+//     the tile would cost twice the LDS reads plus its writes, and LDS bandwidth, not the
+//     matrix cores, bounds this loop on gfx950.  (The FlashMLA walk-through dequantises
+//     to bf16 and runs bf16 MMA with fp32 accumulation, section 计算环节一.)  The scales
+//     are applied in fp32 instead of being rounded into the bf16 values:
+//     S = sum_t scale_t (q_t . k_t) + q_rope . k_rope over the four 128-dim tiles t, and
+//     for the value dims of tile t the probabilities are multiplied by scale_t before PV;
+//   * each wave owns 16 query heads: S^T[32 tok x 16 heads] = K . Q^T with bf16 MFMA
+//     16x16x32 (Q^T resident), an online softmax per head column, and
+//     O^T[512 x 16 heads] += V^T . P^T with V^T read transposed from the FP8 codes
+//     (ds_read_b64_tr_b8); O^T lives in 128 accumulation registers (the register-budget
+//     problem the FlashMLA walk-through describes in section 计算环节二).
+// Operand layouts.  QK row block sb (0, 1) of the A operand holds, in MFMA row m = 4g + r,
+// token 8g + 4sb + r, so lane group g of the S^T result holds tokens 8g..8g+7: exactly the
+// k slots the same lanes feed to the PV MFMA (B = P^T, k = 8g + j), and the transposed
+// read returns tokens 8g..8g+7 of one value dim per lane.  A 16-byte read of the codes
+// feeds two k-steps (dims 64p + 16g + 0..7 and + 8..15), and Q^T is loaded in the same
+// order.
+// With one wave per SIMD nothing else hides a wave's VALU and LDS work behind its
+// MFMAs, so the tile loop is software-pipelined by hand (the FlashMLA walk-through
+// overlaps the softmax of one tile with the matrix products of another across two
+// warpgroups, section 计算环节二; here one wave interleaves the two streams):
+//   top of tile j: the loads of tile j+1 are in; workgroup barrier; loads of tile j+5 out;
+//   phase 1: the QK MFMAs of tile j+1, with the softmax of tile j between them;
+//   phase 2: the PV MFMAs of tile j.
 // The running max is only moved when a tile's max exceeds it by more than 2^8, so the
 // 128-register rescale is rare; probabilities stay below 2^8 and the result is the
 // same up to rounding (the reference cancels in the final normalisation).
@@ -36,13 +51,10 @@
 // Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
 // indices): the items then cover index slots, and slot k of request b names the key
 // position indices[b][k].  The address of a listed token takes two dependent lookups
-// (index, then block table), so they run ahead of the KV loads as per-lane vector loads
-// (lanes 0-7: the wave's 8 tokens): tile j+4's indices and tile j+3's page ids are loaded
-// while tile j is computed, and tile j+2's 8 tokens are gathered by direct-to-LDS loads
-// with per-lane 64-bit addresses (41 chunks per token, 6 instructions per wave).  All of
-// them go through the same in-order load counter as the KV tile, so the wait for tile
-// j+1 also completes the lookups.  A slot outside the item or the request loads a dummy
-// token that the conversion zeroes, and a per-tile bit mask of the real tokens is
+// (index, then block table); lanes 0-7 of each wave (its 8 tokens of a tile) load them
+// direct to LDS, positions 8 tiles and page ids 4 tiles ahead of the tile's own loads,
+// so that every wait for them is one the KV ring does anyway.  A slot outside the item or
+// the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
 // applied in the softmax.
 #include "pa_internal.h"
 
@@ -53,8 +65,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 #define PA_LDS __attribute__((address_space(3)))
 
@@ -66,24 +78,26 @@ constexpr int kDqk = 576, kDv = 512;
 constexpr int kTokBytes = 656;
 constexpr int kChunks = kTokBytes / 16;            // 41 16-byte chunks per token
 constexpr int kT = 32;                             // tokens per tile
-constexpr int kTokPerWave = kT / kWaves;           // 8 tokens loaded / dequantised per wave
-constexpr int kWaveChunks = kTokPerWave * kChunks; // 328
-constexpr int kDmaPerWave = (kWaveChunks + 63) / 64;   // 6 direct-to-LDS loads per wave
-constexpr int kRawTile = kT * kTokBytes;           // 20992
-constexpr int kRawSlots = 3;
-constexpr int kKRow = kDqk * 2 + 16;               // bf16 K row stride (padded) = 1168
-constexpr int kKTile = kT * kKRow;                 // 37376
+constexpr int kTokPerWave = kT / kWaves;           // 8 tokens loaded per wave and tile
+constexpr int kRawRow = 672;                       // LDS row of a token (656 + 16)
+constexpr int kRawTile = kT * kRawRow;             // 21504
+constexpr int kRawSlots = 6;                       // tile ring
+constexpr int kAhead = kRawSlots - 2;              // lookups: page ids 4, positions 8 tiles ahead
+constexpr int kLookRing = 16;                      // lookup slots (tiles) per wave
 constexpr int kKSteps = kDqk / 32;                 // 18 (k = 32 per MFMA)
-constexpr int kDvBlocks = kDv / 16;                // 32
+constexpr int kDvBlocks = kDv / 16;                // 32 PV MFMAs per tile and wave
 constexpr float kLazyMax = 8.0f;                   // log2 units
+
+static_assert(kRawSlots >= 4, "the tile loop keeps tiles j, j+1 and loads in flight");
+static_assert(kLookRing > 2 * kAhead, "lookup ring");
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool SPARSE>
 struct MlaCfg {
-    // loads per wave and tile (sparse: the KV gather plus one index and one page-id load)
-    static constexpr int kDmaPerTile = SPARSE ? kDmaPerWave + 2 : kDmaPerWave;
+    // loads per wave and tile: one per token (sparse: plus one page-id and one index load)
+    static constexpr int kLoadsPerTile = SPARSE ? kTokPerWave + 2 : kTokPerWave;
 };
 
 template <int N>
@@ -93,7 +107,7 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Barrier for LDS handoffs only: this wave's LDS writes are complete, then all waves
+// Barrier for LDS handoffs only: this wave's LDS accesses are complete, then all waves
 // meet.  (A full __syncthreads would also drain the in-flight KV loads.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -103,25 +117,64 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(PA_LDS const void *)p;
 }
 
-__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p)
+// Direct-to-LDS loads, issued as inline asm (M0 = the LDS address of lane 0's data; lane
+// i's goes i * size bytes further).  The compiler then does not see them as LDS writes:
+// it neither makes unrelated LDS accesses wait for them (its alias tracking of such
+// loads gives up across loop iterations and waits for all of them) nor counts them;
+// every wait for them in this file is explicit.  Nothing else here uses M0.
+__device__ __forceinline__ void lds_dma_buf16(__amdgpu_buffer_rsrc_t rs, int voff, uint32_t lds)
 {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PA_LDS bf16x4 *)((PA_LDS uint8_t *)p));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma_glb4(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// 8 e4m3 codes (two words) -> 8 bf16 (exact)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
+{
+    const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 o;
+    o[0] = b0[0]; o[1] = b0[1]; o[2] = b1[0]; o[3] = b1[1];
+    o[4] = b2[0]; o[5] = b2[1]; o[6] = b3[0]; o[7] = b3[1];
+    return o;
+}
+
+// max / sum over the lanes l, l^16, l^32, l^48 (the 4 row groups of one MFMA column),
+// through the row-swap permutes (no LDS); the result is the same in all four lanes
+__device__ __forceinline__ float col_max(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float col_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // SPARSE: index-slot items.  MASKED: a per-wave key range narrower than the item (draft
 // tokens' causal limits, a sliding window); a separate instantiation, because the plain
-// kernel sits at the register-file limit and any extra live value spills.
+// kernel sits near the register-file limit.
 template <bool SPARSE, bool MASKED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void pa_mla_kernel(
     DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ indices)
 {
-    constexpr int kDmaPerTile = MlaCfg<SPARSE>::kDmaPerTile;
+    constexpr int kLoadsPerTile = MlaCfg<SPARSE>::kLoadsPerTile;
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKTile];
-    __shared__ uint32_t s_valid[2];            // sparse: real-token bits of each K buffer
-    // sparse lookups: [position | page id][tile % 4][wave][token]
-    __shared__ int32_t s_look[SPARSE ? 2 * 4 * kWaves * kTokPerWave : 1];
+    __shared__ uint32_t s_valid[kRawSlots];    // sparse: real-token bits of each slot
+    // sparse lookups: [position | page id][tile % 16][wave][token]
+    __shared__ int32_t s_look[SPARSE ? 2 * kLookRing * kWaves * kTokPerWave : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -136,16 +189,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int qi = row0 / G;                       // the wave's draft token (G % 16 == 0)
     const int head0 = row0 - qi * G;               // its first head
     const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
+    const int page_mask = (1 << a.page_shift) - 1;
 
-    // lane byte offset of chunk x = 64 i + lane (token x / 41, chunk x % 41) inside the
-    // 8 token rows a wave loads per tile (the sparse gather recomputes its split)
-    int dma_off[kDmaPerWave];
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; i++) {
-        const int x = 64 * i + lane;
-        const int tt = x / kChunks, c = x - tt * kChunks;
-        dma_off[i] = SPARSE ? 0 : tt * (int)a.s_tok_b + 16 * c;
-    }
+    // LDS byte offsets inside a tile slot: the QK operand rows of row block 0 (token
+    // 8(col/4) + col%4, at this lane's 16 bytes of each 64-dim group; row block 1 is 4
+    // rows further), the scale rows of this lane's tokens 8g4 + j, and the transposed PV
+    // read (lane pair 2r, 2r+1 of a 16-lane block supplies row 8g4 + r, bytes 0-7 and
+    // 8-15 of the block's 16 value dims)
+    const uint32_t qk_off0 = (uint32_t)((8 * (col >> 2) + (col & 3)) * kRawRow + 16 * g4);
+    const uint32_t sc_off = (uint32_t)(8 * g4 * kRawRow + 512);
+    const uint32_t pv_off = (uint32_t)((8 * g4 + ((lane & 15) >> 1)) * kRawRow + 8 * (lane & 1));
 
     const int ib = plan[a.part_begin_off + part];
     const int ie = plan[a.part_begin_off + part + 1];
@@ -164,136 +217,88 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (a.window > 0) tlo = max(0, L - nq + qi - a.window + 1);
         }
 
-        // sparse lookups, lane l: token l % 8 of the wave's 8 in tile j, index slot k.  They
-        // go to shared memory by direct-to-LDS loads (no registers live across the tile
-        // compute; the loads complete in order with the KV gathers) and are read back by
-        // inline asm (which the compiler does not make wait for the gathers in flight).
+        // ---- sparse lookups, lane l < 8: token l of the wave's 8 in tile j, index slot k
         const int Lb = SPARSE ? seq_lens[b] : 0;
         auto sp_slot = [&](int j) { return t0 + kT * j + kTokPerWave * wave + (lane & 7); };
-        auto sp_ok = [&](int j, int pos) { return sp_slot(j) < t1 && pos >= 0 && pos < Lb; };
-        auto look = [&](int which, int j) { return &s_look[((which * 4 + (j & 3)) * kWaves + wave) * kTokPerWave]; };
+        auto look = [&](int which, int j) {
+            return &s_look[((which * kLookRing + (j & (kLookRing - 1))) * kWaves + wave) * kTokPerWave];
+        };
         auto sp_issue_pos = [&](int j) {           // slots past the row: its last entry
             if (lane < kTokPerWave)
-                __builtin_amdgcn_global_load_lds((const void *)(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1)),
-                                                 (PA_LDS void *)look(0, j), 4, 0, 0);
+                lds_dma_glb4(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1), lds_addr(look(0, j)));
         };
         auto sp_issue_page = [&](int j, int pos) { // no real token: the row's first page
+            const bool ok = sp_slot(j) < t1 && pos >= 0 && pos < Lb;
             if (lane < kTokPerWave)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(bt + (int64_t)b * a.max_pages + (sp_ok(j, pos) ? pos >> a.page_shift : 0)),
-                    (PA_LDS void *)look(1, j), 4, 0, 0);
+                lds_dma_glb4(bt + (int64_t)b * a.max_pages + (ok ? pos >> a.page_shift : 0), lds_addr(look(1, j)));
         };
-        auto sp_read = [&](int which, int j) {     // issue only: complete after lgkm_wait
+        auto sp_read = [&](int which, int j) {     // a lookup that is in; lane l: token l % 8
             int v;
-            asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(lds_addr(look(which, j)) + 4 * (lane & 7)));
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v)
+                         : "v"(lds_addr(look(which, j)) + 4 * (lane & 7)) : "memory");
             return v;
         };
-        auto lgkm_wait = [](int &x, int &y, int &z) {
-            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z)::"memory");
-        };
 
-        // ---- direct-to-LDS load of this wave's 8 tokens of tile j into raw slot s (buffer
-        //      loads over the 8 token rows: one 32-bit lane offset per instruction)
-        // sparse: gather of the wave's 8 listed tokens of tile j (position pos and page id
-        // page in lane l % 8) into raw slot s; returns the bits of the real tokens.  A
-        // token that is not real loads the first token of page 0 instead.
-        auto dma_sparse = [&](int j, int s, int pos, int page) {
-            const bool ok = sp_ok(j, pos);
-            const int64_t off = ok ? (int64_t)page * a.s_page_b +
-                                         (int64_t)(pos & ((1 << a.page_shift) - 1)) * a.s_tok_b
-                                   : 0;
-            const int lo = (int)(uint32_t)off, hi = (int)(off >> 32);
-            uint8_t *dst = &raw[s][wave * kWaveChunks * 16];
+        // ---- loads of tile t into its ring slot: token tt of the wave (tile row 8 wave +
+        //      tt) by lanes 0-40 through a buffer resource over that token's 656 bytes, or
+        //      over none (reads as zeros) when it is not real.  Sparse: the page ids of tile
+        //      t + kAhead and the positions of tile t + 2 kAhead go out first; the lookups
+        //      this uses were loaded kAhead tiles ago.
+        // dense: page id of the wave's first token of the next tile to load (tile 0 here)
+        int next_page = SPARSE ? 0 : bt[(int64_t)b * a.max_pages + (min(t0 + kTokPerWave * wave, t1 - 1) >> a.page_shift)];
+        auto issue_tile = [&](int t) {
+            uint8_t *dst = &raw[t % kRawSlots][kTokPerWave * wave * kRawRow];
+            if (SPARSE) {
+                const int pos_look = sp_read(0, t + kAhead);
+                sp_issue_page(t + kAhead, pos_look);
+                sp_issue_pos(t + 2 * kAhead);
+                const int pos = sp_read(0, t), page = sp_read(1, t);
+                uint32_t vm = 0;
 #pragma unroll
-            for (int i = 0; i < kDmaPerWave; i++) {
-                // chunk x = 64 i + lane: token x / 41 (as x * 1599 >> 16, exact for x < 1681)
-                const int x = 64 * i + lane;
-                const int tt = (x * 1599) >> 16, c = x - kChunks * tt;
-                const uint32_t tlo = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * tt, lo);
-                const uint32_t thi = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * tt, hi);
-                const uint8_t *g = a.k_pool + (int64_t)(((uint64_t)thi << 32) | tlo) + 16 * c;
-                if (64 * i + lane < kWaveChunks)
-                    __builtin_amdgcn_global_load_lds((const void *)g, (PA_LDS void *)(dst + 64 * 16 * i), 16,
-                                                     0, 0);
-            }
-            return (uint32_t)__ballot(ok) & 0xFFu;
-        };
-
-        auto dma_tile = [&](int j, int s) {
-            const int jc = j < ntiles ? j : ntiles - 1;     // past the end: reload the last tile
-            int tw = t0 + kT * jc + kTokPerWave * wave;     // first of the wave's 8 tokens
-            if (tw >= t1) tw = (t1 - 1) & ~(kTokPerWave - 1);
-            const int page = bt[(int64_t)b * a.max_pages + (tw >> a.page_shift)];
-            const int slot0 = tw & ((1 << a.page_shift) - 1);
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a.k_pool + (int64_t)page * a.s_page_b + (int64_t)slot0 * a.s_tok_b), (short)0,
-                kTokPerWave * (int)a.s_tok_b, 0x00020000);
-            uint8_t *dst = &raw[s][wave * kWaveChunks * 16];
+                for (int tt = 0; tt < kTokPerWave; tt++) {
+                    const int p = __builtin_amdgcn_readlane(pos, tt);
+                    const int pg = __builtin_amdgcn_readlane(page, tt);
+                    const int k = t0 + kT * t + kTokPerWave * wave + tt;
+                    const bool ok = k < t1 && p >= 0 && p < Lb;
+                    vm |= (ok ? 1u : 0u) << tt;
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0)),
+                        (short)0, ok ? kTokBytes : 0, 0x00020000);
+                    if (lane < kChunks) lds_dma_buf16(rs, 16 * lane, lds_addr(dst + tt * kRawRow));
+                }
+                if (lane == 0) ((uint8_t *)&s_valid[t % kRawSlots])[wave] = (uint8_t)vm;
+            } else {
+                const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 8 tokens
+                const int page = next_page;
+                // the next tile's page id, loaded now and used one tile later
+                next_page = bt[(int64_t)b * a.max_pages + (min(tw + kT, t1 - 1) >> a.page_shift)];
+                const uint8_t *pbase = a.k_pool + (int64_t)page * a.s_page_b;
 #pragma unroll
-            for (int i = 0; i < kDmaPerWave; i++) {
-                if (64 * i + lane < kWaveChunks)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void *)(dst + 64 * 16 * i), 16,
-                                                             dma_off[i], 0, 0, 0);
+                for (int tt = 0; tt < kTokPerWave; tt++) {
+                    const bool ok = tw + tt < t1;
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void *)(pbase + (int64_t)((tw + tt) & page_mask) * a.s_tok_b), (short)0,
+                        ok ? kTokBytes : 0, 0x00020000);
+                    if (lane < kChunks) lds_dma_buf16(rs, 16 * lane, lds_addr(dst + tt * kRawRow));
+                }
             }
         };
 
-        // ---- convert this wave's 8 tokens of raw slot s into K tile buffer kb.  Lane l
-        //      converts latent dims 8l..8l+7 of one token per round (8-byte reads, 16-byte
-        //      writes: 16 neighbouring lanes touch 256 contiguous bytes, no bank conflicts);
-        //      then the rope chunks (lane: token l / 8, chunk l % 8) and the 4 tile scales
-        //      (lanes 0-7, into the row padding).  Rows of tokens >= t1 become 0.
-        //      Sparse: vm holds the bits of the wave's real tokens (byte `wave` of the
-        //      tile's mask); the other rows become 0.
-        auto dequant_tile = [&](int j, int s, int kb, uint32_t vm) {
-            const int row0 = kTokPerWave * wave;
-            const int tbase = t0 + kT * j + row0;
-            auto dead = [&](int tt) { return SPARSE ? ((vm >> tt) & 1u) == 0 : tbase + tt >= t1; };
-            if (SPARSE && lane == 0) ((uint8_t *)&s_valid[kb])[wave] = (uint8_t)vm;
-            // the raw slot is read by inline asm: the compiler cannot tell these reads from
-            // the direct-to-LDS writes of later tiles still in flight, and before plain
-            // reads it would wait for those too (all loads of this wave), emptying the ring
-            const uint32_t rbase = lds_addr(&raw[s][row0 * kTokBytes]);
-            uint64_t w[kTokPerWave];
-            u32x4 rope, scl;
-#pragma unroll
-            for (int tt = 0; tt < kTokPerWave; tt++)
-                asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(w[tt]) : "v"(rbase + 8 * lane), "n"(tt * kTokBytes));
-            asm volatile("ds_read_b128 %0, %1 offset:528" : "=v"(rope)
-                         : "v"(rbase + (lane >> 3) * kTokBytes + 16 * (lane & 7)));
-            asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(scl) : "v"(rbase + (lane & 7) * kTokBytes));
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),
-                           "+v"(w[6]), "+v"(w[7]), "+v"(rope), "+v"(scl)::"memory");
-#pragma unroll
-            for (int tt = 0; tt < kTokPerWave; tt++) {
-                const int lo = (int)(uint32_t)w[tt], hi = (int)(w[tt] >> 32);
-                bf16x8 o;
-                const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-                const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-                const bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-                const bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-                o[0] = b0[0]; o[1] = b0[1]; o[2] = b1[0]; o[3] = b1[1];
-                o[4] = b2[0]; o[5] = b2[1]; o[6] = b3[0]; o[7] = b3[1];
-                if (dead(tt)) o = bf16x8{};
-                *(bf16x8 *)(&ktile[kb][(row0 + tt) * kKRow + 16 * lane]) = o;
-            }
-            {
-                const int tt = lane >> 3, c = lane & 7;
-                if (dead(tt)) rope = u32x4{0, 0, 0, 0};
-                *(u32x4 *)(&ktile[kb][(row0 + tt) * kKRow + (512 + 8 * c) * 2]) = rope;
-            }
-            if (lane < kTokPerWave) {
-                if (dead(lane)) scl = u32x4{0, 0, 0, 0};
-                *(u32x4 *)(&ktile[kb][(row0 + lane) * kKRow + kDqk * 2]) = scl;
-            }
-        };
-
-        // ---- Q^T operand of this wave's 32 heads (B of the 32x32x16 MFMA), resident
+        // ---- Q^T operand of this wave's 16 heads (B of the MFMA), resident, in the k order
+        //      of the code reads: step 2p + h <- dims 64p + 16g4 + 8h .. +7 (p < 8), step
+        //      16 + r <- rope dims 512 + 32r + 8g4 .. +7.  A wave with no query rows runs
+        //      the same instruction stream on a zero Q; it writes nothing.
         bf16x8 qop[kKSteps];
         if (active) {
             const uint16_t *qrow = a.q + (((int64_t)b * nq + qi) * Hq + head0 + col) * kDqk;
 #pragma unroll
-            for (int s = 0; s < kKSteps; s++) qop[s] = *(const bf16x8 *)(qrow + 32 * s + 8 * g4);
+            for (int s = 0; s < kKSteps; s++) {
+                const int d = s < 16 ? 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : 512 + 32 * (s - 16) + 8 * g4;
+                qop[s] = *(const bf16x8 *)(qrow + d);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kKSteps; s++) qop[s] = bf16x8{};
         }
 
         f32x4 acc[kDvBlocks];
@@ -302,166 +307,211 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         float m = -INFINITY;     // reference max (log2 domain) of head `col`
         float l = 0.f;
 
-        if (ntiles > 0) {
-            // sparse pipeline at the top of tile j: the positions of tiles j+2 and j+3 and
-            // the page ids of tile j+2 are in shared memory, vm1 = real-token bits of j+1
-            uint32_t vm0 = 0, vm1 = 0, vm2 = 0;
-            if (SPARSE) {
-                // positions of tiles 0-3, page ids of tiles 0-2, gathers of tiles 0 and 1
-                for (int t = 0; t < 4; t++) sp_issue_pos(t);
-                wait_vmcnt<0>();
-                int p0 = sp_read(0, 0), p1 = sp_read(0, 1), p2 = sp_read(0, 2);
-                lgkm_wait(p0, p1, p2);
-                sp_issue_page(0, p0);
-                sp_issue_page(1, p1);
-                sp_issue_page(2, p2);
-                wait_vmcnt<0>();
-                int g0 = sp_read(1, 0), g1 = sp_read(1, 1), unused = 0;
-                lgkm_wait(g0, g1, unused);
-                vm0 = dma_sparse(0, 0, p0, g0);
-                vm1 = dma_sparse(1, 1, p1, g1);
-                wait_vmcnt<kDmaPerWave>();        // tile 0 done (tile 1's gather is younger)
-            } else {
-                dma_tile(0, 0);
-                dma_tile(1, 1);
-                wait_vmcnt<kDmaPerTile>();        // own loads of tile 0 done
+        // ---- S^T of tile t (rows: this lane's tokens 8g4 + 4sb + r, r = 0..3): one partial
+        //      per 128-dim scale tile (k-steps 4t'..4t'+3) and one for the rope dims
+        //      (k-steps 16, 17), combined with the token scales in fp32.  inter(k) runs
+        //      right after MFMA k (k = 0..35), with nothing moved across it.
+        auto qk_tile = [&](int t, float (&st)[8], auto &&inter) {
+            const uint8_t *slot = raw[t % kRawSlots];
+#pragma unroll
+            for (int sb = 0; sb < 2; sb++) {
+                f32x4 part[5];
+#pragma unroll
+                for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const uint8_t *kbase = slot + qk_off0 + 4 * sb * kRawRow;
+                // read q < 8: 16 bytes of codes (k-steps 2q, 2q+1); q = 8, 9: 16 bytes of
+                // rope (k-step 8 + q)
+                auto rd = [&](int q) {
+                    return *(const u32x4 *)(kbase + (q < 8 ? 64 * q : 528 + 64 * (q - 8)));
+                };
+                // the A operand of k-step ks from read q = ks / 2 (ks < 16) or ks - 8
+                auto kop_of = [](int ks, const u32x4 &v) {
+                    if (ks >= 16) return __builtin_bit_cast(bf16x8, v);
+                    return (ks & 1) ? fp8x8_to_bf16(v[2], v[3]) : fp8x8_to_bf16(v[0], v[1]);
+                };
+                auto q_of = [](int ks) { return ks < 16 ? ks >> 1 : ks - 8; };
+                u32x4 w[3];
+                w[0] = rd(0);
+                w[1] = rd(1);
+                // operands are converted one MFMA ahead (no VALU-to-MFMA wait states)
+                bf16x8 kop[2];
+                kop[0] = kop_of(0, w[0]);
+#pragma unroll
+                for (int ks = 0; ks < kKSteps; ks++) {
+                    const int q = q_of(ks);
+                    const bool first = ks < 16 ? (ks & 1) == 0 : true;
+                    if (first && q + 2 < 10) w[(q + 2) % 3] = rd(q + 2);
+                    const int p = ks < 16 ? ks / 4 : 4;
+                    part[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks & 1], qop[ks], part[p], 0, 0, 0);
+                    if (ks + 1 < kKSteps) kop[(ks + 1) & 1] = kop_of(ks + 1, w[q_of(ks + 1) % 3]);
+                    inter(kKSteps * sb + ks);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const f32x4 sc = *(const f32x4 *)(slot + sc_off + (4 * sb + r) * kRawRow);
+                    float x = part[4][r];
+#pragma unroll
+                    for (int p = 0; p < 4; p++) x += sc[p] * part[p][r];
+                    st[4 * sb + r] = x;
+                }
             }
-            dequant_tile(0, 0, 0, vm0);
+        };
+
+        // ---- softmax of tile j (S^T in st) in steps, k = 0..kSmSteps-1: logits and mask,
+        //      the max over the head's 32 tokens, the lazily moved reference m_new,
+        //      p = 2^(s - m_new) and their sum ps
+        float sv[8], bm = -INFINITY, m_new = m, pr[8], ps = 0.f;
+        auto sm_step = [&](int j, const float (&st)[8], int k) {
+            switch (k) {
+            case 0: {
+                const uint32_t vmask = SPARSE ? s_valid[j % kRawSlots] : 0u;
+                bm = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 8; r++) {
+                    const int row = 8 * g4 + r;                 // token within the tile
+                    const int tok = t0 + kT * j + row;
+                    const bool vis = SPARSE ? ((vmask >> row) & 1u) != 0
+                                            : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
+                    sv[r] = vis ? st[r] * a.scale_log2 : -INFINITY;
+                    bm = fmaxf(bm, sv[r]);
+                }
+                break;
+            }
+            case 2:
+                bm = col_max(bm);
+                m_new = bm > m + kLazyMax ? bm : m;
+                break;
+            case 4:
+            case 6: {
+                const float mref = m_new == -INFINITY ? 0.f : m_new;
+                const int r0 = k == 4 ? 0 : 4;
+#pragma unroll
+                for (int r = r0; r < r0 + 4; r++) {
+                    pr[r] = fast_exp2(sv[r] - mref);
+                    asm volatile("" : "+v"(pr[r]));       // computed here, not after the branch
+                }
+                break;
+            }
+            case 8:
+                ps = 0.f;
+#pragma unroll
+                for (int r = 0; r < 8; r++) ps += pr[r];
+                break;
+            default:
+                break;
+            }
+        };
+        constexpr int kSmSteps = 9;
+
+        // ---- O^T += V^T . P^T for tile j: A = V^T from the transposed code read (this
+        //      lane: value dim 16db + col, tokens 8g4 + 0..7), B = P^T times the value
+        //      tile's token scales (pbt[t], built 3 MFMAs before MFMA 8t from scales read
+        //      4 MFMAs before that)
+        auto pv_tile = [&](int j) {
+            const uint8_t *slot = raw[j % kRawSlots];
+            const uint8_t *vbase = slot + pv_off;
+            bf16x8 pbt[4];
+            float scv[8];
+            auto scale_read = [&](int t) {         // tile t's scales of this lane's 8 tokens
+#pragma unroll
+                for (int r = 0; r < 8; r++) scv[r] = *(const float *)(slot + sc_off + r * kRawRow + 4 * t);
+            };
+            auto p_times_scale = [&](int t) {
+#pragma unroll
+                for (int r = 0; r < 8; r++) pbt[t][r] = (__bf16)(pr[r] * scv[r]);
+            };
+            auto rd = [&](int db) {
+                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2 *)(PA_LDS uint8_t *)(vbase + 16 * db));
+            };
+            i32x2 vw[3];
+            scale_read(0);
+            vw[0] = rd(0);
+            vw[1] = rd(1);
+            p_times_scale(0);
+            bf16x8 va[2];
+            va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
+#pragma unroll
+            for (int db = 0; db < kDvBlocks; db++) {
+                if (db + 2 < kDvBlocks) vw[(db + 2) % 3] = rd(db + 2);
+                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db & 1], pbt[db >> 3], acc[db], 0, 0, 0);
+                if (db + 1 < kDvBlocks)
+                    va[(db + 1) & 1] = fp8x8_to_bf16((uint32_t)vw[(db + 1) % 3][0], (uint32_t)vw[(db + 1) % 3][1]);
+                if ((db & 7) == 1 && db < 24) scale_read((db >> 3) + 1);
+                if ((db & 7) == 5 && db < 24) p_times_scale((db >> 3) + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        if (ntiles > 0) {
+            // ---- prologue: lookups (sparse), the loads of tiles 0..kRawSlots-2, S^T of
+            //      tile 0
+            if (SPARSE) {
+                for (int t = 0; t < 2 * kAhead; t++) sp_issue_pos(t);
+                wait_vmcnt<0>();
+                for (int t = 0; t < kAhead; t++) sp_issue_page(t, sp_read(0, t));
+                wait_vmcnt<0>();
+            }
+#pragma unroll
+            for (int t = 0; t < kRawSlots - 1; t++) {
+                // tile t's lookups came from tile t - kAhead's loads
+                if (SPARSE && t >= kAhead) wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
+                issue_tile(t);
+            }
+            wait_vmcnt<(kRawSlots - 2) * kLoadsPerTile>();   // tile 0 in
             lds_barrier();
 
+            float st[8], st_next[8];
+            qk_tile(0, st, [](int) {});
+
             // The tile loop never rescales O^T itself: when a tile's max exceeds the
-            // reference by more than 2^8 it leaves (before that tile's PV), the rescale
-            // runs outside, and the loop resumes at the same tile.  Inside the loop O^T is
-            // only touched by MFMAs, so it stays in the accumulation registers.
+            // reference by more than 2^8 it leaves after phase 1, the rescale runs outside,
+            // and the loop redoes phase 1 of the same tile with the new reference.  Inside
+            // the loop O^T is only touched by MFMAs, so it stays in the accumulation
+            // registers.
             int j = 0;
-            int dma_next = 2;                     // next tile whose loads are not issued yet
-            float bm_exit = -INFINITY;
+            bool redo = false;
             for (;;) {
             for (; j < ntiles; j++) {
-                // tile j+2's loads go out before the compute of tile j (once per tile, also
-                // when the loop resumes at j after a rescale)
-                if (dma_next == j + 2) {
-                    if (SPARSE) {
-                        // the previous tile's lookups are done (tile j+1's gather is
-                        // younger); issue tile j+3's page ids and tile j+4's positions
-                        // (the next tile waits for these, not for this tile's KV), then
-                        // the gather of tile j+2
-                        wait_vmcnt<kDmaPerWave>();
-                        int p3 = sp_read(0, j + 3), p2 = sp_read(0, j + 2), g2 = sp_read(1, j + 2);
-                        lgkm_wait(p3, p2, g2);
-                        sp_issue_page(j + 3, p3);
-                        sp_issue_pos(j + 4);
-                        vm2 = dma_sparse(j + 2, (j + 2) % kRawSlots, p2, g2);
-                    } else {
-                        dma_tile(j + 2, (j + 2) % kRawSlots);
-                    }
-                    dma_next++;
+                if (!redo) {
+                    // ---- top: tile j+1's loads in (tiles j+2.. are younger), all waves
+                    //      past tile j-1, then tile j+kRawSlots-1's loads into its slot
+                    wait_vmcnt<(kRawSlots - 3) * kLoadsPerTile>();
+                    lds_barrier();
+                    issue_tile(j + kRawSlots - 1);
                 }
-                const uint8_t *kt = ktile[j & 1];
-
-                if (active) {
-                    // ---- S^T = K . Q^T for the two 16-token row blocks (rows 16sb + 4g4 + r):
-                    //      one partial per 128-dim scale tile (k-steps 4t..4t+3) and one for
-                    //      the rope dims (k-steps 16, 17), combined with the tile scales in fp32
-                    // Per 16-token row block: 18 MFMA steps whose K operand is read from LDS
-                    // two steps ahead; the scheduling barriers pin that order (one wave per
-                    // SIMD: nothing else hides the LDS latency).
-                    f32x4 st[2];
-                    f32x4 sc4[2][4];       // scales of this lane's 8 tokens: [sb][r] -> 4 tiles
+                redo = false;
+                // ---- phase 1: QK of tile j+1 (after the last tile: a dummy on the next
+                //      slot), the softmax of tile j between its MFMAs
+                qk_tile(j + 1, st_next, [&](int k) {
+                    if (k < kSmSteps) sm_step(j, st, k);
+                });
+                if (__any(m_new != m)) break;
+                l += ps;
+                // ---- phase 2: PV of tile j
+                pv_tile(j);
 #pragma unroll
-                    for (int sb = 0; sb < 2; sb++) {
-                        f32x4 part[5];
-#pragma unroll
-                        for (int t = 0; t < 5; t++) part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        const uint8_t *kbase = kt + (16 * sb + col) * kKRow + 16 * g4;
-                        bf16x8 kf[3];
-                        kf[0] = *(const bf16x8 *)kbase;
-                        kf[1] = *(const bf16x8 *)(kbase + 64);
-#pragma unroll
-                        for (int ks = 0; ks < kKSteps; ks++) {
-                            if (ks + 2 < kKSteps) kf[(ks + 2) % 3] = *(const bf16x8 *)(kbase + 64 * (ks + 2));
-                            const int t = ks < 16 ? ks / 4 : 4;
-                            part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3], qop[ks], part[t], 0, 0, 0);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; r++) {
-                            sc4[sb][r] = *(const f32x4 *)(kt + (16 * sb + 4 * g4 + r) * kKRow + kDqk * 2);
-                            float x = part[4][r];
-#pragma unroll
-                            for (int t = 0; t < 4; t++) x += sc4[sb][r][t] * part[t][r];
-                            st[sb][r] = x;
-                        }
-                    }
-                    // ---- online softmax with a lazily moved reference
-                    float bm = -INFINITY;
-                    float sv[8];
-                    const uint32_t vmask = SPARSE ? s_valid[j & 1] : 0u;
-#pragma unroll
-                    for (int r = 0; r < 8; r++) {
-                        const int row = 16 * (r >> 2) + 4 * g4 + (r & 3);
-                        const int tok = t0 + kT * j + row;
-                        const bool vis = SPARSE ? ((vmask >> row) & 1u) != 0
-                                                : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
-                        sv[r] = vis ? st[r >> 2][r & 3] * a.scale_log2 : -INFINITY;
-                        bm = fmaxf(bm, sv[r]);
-                    }
-                    bm = fmaxf(bm, __shfl_xor(bm, 16));
-                    bm = fmaxf(bm, __shfl_xor(bm, 32));
-                    if (__any(bm > m + kLazyMax)) {
-                        bm_exit = bm;
-                        break;
-                    }
-                    const float mref = m == -INFINITY ? 0.f : m;
-                    bf16x8 pbt[4];         // P times the scale of value tile t, per token
-                    float ps = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 8; r++) {
-                        const float pr = fast_exp2(sv[r] - mref);
-                        ps += pr;
-#pragma unroll
-                        for (int t = 0; t < 4; t++) pbt[t][r] = (__bf16)(pr * sc4[r >> 2][r & 3][t]);
-                    }
-                    l += ps;
-                    // ---- O^T += V^T . P^T; k = 8g4 + r <-> token (r < 4 ? 4g4 + r : 16 + 4g4 + r - 4)
-                    const uint8_t *vbase = kt + (4 * g4 + (col >> 2)) * kKRow + 4 * (col & 3) * 2;
-                    auto read_vt = [&](int db) {
-                        const bf16x4 lo = lds_tr16(vbase + 32 * db);
-                        const bf16x4 hi = lds_tr16(vbase + 16 * kKRow + 32 * db);
-                        bf16x8 va;
-#pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            va[e] = lo[e];
-                            va[4 + e] = hi[e];
-                        }
-                        return va;
-                    };
-                    bf16x8 vf[3];
-                    vf[0] = read_vt(0);
-                    vf[1] = read_vt(1);
-#pragma unroll
-                    for (int db = 0; db < kDvBlocks; db++) {
-                        if (db + 2 < kDvBlocks) vf[(db + 2) % 3] = read_vt(db + 2);
-                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db % 3], pbt[db >> 3], acc[db], 0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                // ---- next tile: own loads of tile j+1 done (tile j+2's are younger), then
-                //      dequantise it into the other K buffer
-                wait_vmcnt<kDmaPerTile>();
-                dequant_tile(j + 1, (j + 1) % kRawSlots, (j + 1) & 1, vm1);
-                vm1 = vm2;
-                lds_barrier();
+                for (int r = 0; r < 8; r++) st[r] = st_next[r];
             }
             if (j >= ntiles) break;
-            // move the reference to this tile's max and rescale (rare); tile j is redone
+            // move the reference to m_new and rescale (rare; every item's first tile).
+            // The multiply reads and writes O^T in place, so it stays in the accumulation
+            // registers (a plain multiply would make the compiler copy all of O^T out).
             {
-                const float mn = fmaxf(m, bm_exit);
-                const float alpha = fast_exp2(m - mn);   // m = -inf: 0
-                m = mn;
-                l *= alpha;
+                const float alpha = fast_exp2(m - m_new);    // m = -inf: 0
+                m = m_new;
+                l = l * alpha;
 #pragma unroll
-                for (int i = 0; i < kDvBlocks; i++) acc[i] *= alpha;
+                for (int i = 0; i < kDvBlocks; i++) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        float v = acc[i][e], tmp;
+                        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                                     : "+a"(v), "=&v"(tmp) : "v"(alpha));
+                        acc[i][e] = v;
+                    }
+                }
+                redo = true;
             }
             }
             wait_vmcnt<0>();
@@ -469,8 +519,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
         // ---- epilogue: this wave's heads are complete for this item
         if (active) {
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+            l = col_sum(l);
             const int head = head0 + col;
             float inv, lse_v;
             const float sk = (a.sinks && (flags & 1)) ? a.sinks[head] * 1.4426950408889634f : -INFINITY;
