@@ -272,14 +272,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const int page = next_page;
                 // the next tile's page id, loaded now and used one tile later
                 next_page = bt[(int64_t)b * a.max_pages + (min(tw + kT, t1 - 1) >> a.page_shift)];
-                const uint8_t *pbase = a.k_pool + (int64_t)page * a.s_page_b;
+                // the 8 tokens are consecutive slots of one page: one 64-bit address, then
+                // one stride step per token
+                const uint8_t *tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
+                const int nreal = min(max(t1 - tw, 0), kTokPerWave);
+                const uint32_t lds0 = lds_addr(dst);
 #pragma unroll
                 for (int tt = 0; tt < kTokPerWave; tt++) {
-                    const bool ok = tw + tt < t1;
                     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                        (void *)(pbase + (int64_t)((tw + tt) & page_mask) * a.s_tok_b), (short)0,
-                        ok ? kTokBytes : 0, 0x00020000);
-                    if (lane < kChunks) lds_dma_buf16(rs, 16 * lane, lds_addr(dst + tt * kRawRow));
+                        (void *)tok, (short)0, tt < nreal ? kTokBytes : 0, 0x00020000);
+                    if (lane < kChunks) lds_dma_buf16(rs, 16 * lane, lds0 + tt * kRawRow);
+                    tok += a.s_tok_b;
                 }
             }
         };
