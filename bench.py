@@ -9,8 +9,12 @@ Hq=64, Hkv=8, D=128, bf16 KV, 64-token pages, 4096 tokens each, balanced plan).
 
 Prints ONE JSON line.  `value` is the achieved algorithmic KV bandwidth (GB/s) of a
 whole step; `roofline` is for the dominant kernel (the decode kernel), timed with
-HIP events on the launch stream; `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workload.
+HIP events on the launch stream over a graph of back-to-back launches (its device
+time; eager launches of a small kernel time the host's launch rate instead);
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+A workload whose KV pool fits in the 256 MB last-level cache is also timed cold
+(`cold`: each step reads the next of enough pool copies to exceed 512 MB), and its
+roofline figure is the cold one.
 """
 import argparse
 import json
@@ -58,6 +62,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
+    ap.add_argument("--cold-copies", type=int, default=-1,
+                    help="also time with each step reading the next of N copies of the KV pool "
+                         "(so that the pool is not cache-resident); -1: automatic (enough copies "
+                         "to exceed 512 MB when one pool fits in the 256 MB last-level cache), 0: off")
     ap.add_argument("--fused-combine", action="store_true",
                     help="merge chunks inside the decode kernel (last workgroup per request) "
                          "instead of the combine kernel")
@@ -151,7 +159,7 @@ def main():
     runner.combine(out, lse)
     torch.cuda.synchronize()
 
-    graph_us = None
+    graph_us = decode_graph_us = None
     if not args.no_graph:
         # several steps per graph, so that the per-replay launch cost is amortised and
         # the figure is the device time of a step
@@ -177,26 +185,60 @@ def main():
         g1.record()
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1000.0 / (reps * per_graph)
+        # the decode kernel alone, launched from a graph: its device time without the host's
+        # per-launch cost (which is what eager back-to-back launches of a small kernel time)
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd):
+            for _ in range(per_graph):
+                runner.run(q, kp, vp, bt, sl, out, lse, k_scale=ks, v_scale=vs, indices=idx)
+        gd.replay()
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(reps):
+            gd.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        decode_graph_us = g0.elapsed_time(g1) * 1000.0 / (reps * per_graph)
+        runner.combine(out, lse)
+        torch.cuda.synchronize()
+
+    cold = None
+    pool_bytes = sum(t.numel() * t.element_size() for t in (kp, vp, ks, vs) if t is not None)
+    ncold = args.cold_copies
+    if ncold < 0:
+        ncold = min(-(-(512 << 20) // pool_bytes) + 1, 1024) if pool_bytes < (256 << 20) else 0
+    if ncold > 0:
+        cold = cold_timing(runner, case, ncold, args, (q, kp, vp, ks, vs, bt, sl, out, lse, idx), stream)
 
     kv_bytes = synth.kv_bytes(case)
     io = synth.io_bytes(case)
     step_us = step_ms * 1000.0
     gbs = kv_bytes / (step_us * 1e-6) / 1e9
-    dec_gbs = kv_bytes / (decode_us * 1e-6) / 1e9
+    # the dominant kernel's time per launch: from a graph of launches when timed (device
+    # time), else from eager back-to-back launches
+    kern_us = decode_us if decode_graph_us is None else decode_graph_us
+    dec_gbs = kv_bytes / (kern_us * 1e-6) / 1e9
     fmt = {0: "bf16", 1: "fp8e4m3-kv/bf16", 2: "mla656-fp8/bf16"}[case["kv_format"]]
 
     traffic = counter_traffic(case["name"], B) if args.q_len == 1 and not args.topk else None
     if case["kv_format"] == 2:
         # MLA: 128 heads share each token, so the contraction is MFMA-bound
+        kern_us = kern_us if cold is None else (cold["decode_kernel_graph_us"] or cold["decode_kernel_us"])
         tokens = kv_bytes / synth.MLA_TOKEN_BYTES      # attended keys (listed ones if sparse)
-        tflops = MLA_FLOP_PER_TOKEN * args.q_len * tokens / (decode_us * 1e-6) / 1e12
+        tflops = MLA_FLOP_PER_TOKEN * args.q_len * tokens / (kern_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "pa_mla_kernel"}
+                "traffic": traffic, "kernel": "pa_mla_kernel",
+                "timing": "warm, " + ("eager launches" if decode_graph_us is None else "graph of launches")}
     else:
-        roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "pa_decode_kernel<%d,%s>" % (case["D"], "bf16" if case["kv_format"] == 0 else "fp8")}
+        # a pool that fits in the last-level cache is quoted against HBM only cold
+        cold_us = None if cold is None else (cold["decode_kernel_graph_us"] or cold["decode_kernel_us"])
+        roof_gbs = dec_gbs if cold is None else kv_bytes / (cold_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(roof_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(roof_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "pa_decode_kernel<%d,%s>" % (case["D"], "bf16" if case["kv_format"] == 0 else "fp8"),
+                "timing": ("warm" if cold is None else "cold (%d rotating pool copies)" % cold["copies"])
+                          + (", eager launches" if decode_graph_us is None else ", graph of launches")}
     roof["algorithmic_bytes"] = kv_bytes
 
     cpu = None
@@ -229,12 +271,93 @@ def main():
         "io_bytes_per_step": io,
         "plan_us": round(plan_us, 2),
         "decode_kernel_us": round(decode_us, 2),
+        "decode_kernel_graph_us": None if decode_graph_us is None else round(decode_graph_us, 2),
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
         "wall_s_timed": round(wall_s, 4),
         "roofline": roof,
+        "cold": None if cold is None else dict(cold, kv_gbs_step=round(kv_bytes / (cold["us_per_step"] * 1e-6) / 1e9, 1),
+                                               pct_of_hbm_peak_step=round(100.0 * kv_bytes / (cold["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def cold_timing(runner, case, ncopies, args, bufs, stream):
+    """The step, the decode kernel and a graph of steps, each step reading the next of
+    `ncopies` copies of the KV pool (and scales): with more bytes than the last-level
+    cache holds, every step's KV comes from HBM."""
+    import torch
+
+    q, kp, vp, ks, vs, bt, sl, out, lse, idx = bufs
+    copies = [tuple(None if t is None else t.clone() for t in (kp, vp, ks, vs)) for _ in range(ncopies)]
+    torch.cuda.synchronize()
+
+    def run(i):
+        k, v, a, b = copies[i % ncopies]
+        runner.run(q, k, v, bt, sl, out, lse, k_scale=a, v_scale=b, indices=idx)
+
+    def step(i):
+        run(i)
+        runner.combine(out, lse)
+
+    n = max(args.steps, 2 * ncopies)
+    for i in range(ncopies):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1000.0 / n
+    e0.record(stream)
+    for i in range(n):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1000.0 / n
+    graph_us = dec_graph_us = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(ncopies):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, n // ncopies)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1000.0 / (reps * ncopies)
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd):
+            for i in range(ncopies):
+                run(i)
+        gd.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            gd.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_graph_us = e0.elapsed_time(e1) * 1000.0 / (reps * ncopies)
+        runner.combine(out, lse)
+        torch.cuda.synchronize()
+    pool = sum(t.numel() * t.element_size() for t in copies[0] if t is not None)
+    del copies
+    torch.cuda.empty_cache()
+    return {"copies": ncopies, "bytes_rotated": pool * ncopies, "us_per_step": round(step_us, 2),
+            "decode_kernel_us": round(dec_us, 2), "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
+            "decode_kernel_graph_us": None if dec_graph_us is None else round(dec_graph_us, 2)}
 
 
 def cpu_baseline(case, seconds):
