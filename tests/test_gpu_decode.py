@@ -263,6 +263,8 @@ MLA_SMALL = [
     dict(lens=(129, 2000), G=64, P=16),
     dict(lens=(31, 32, 33), G=16, P=32, splits=2),
     dict(lens=(0, 100, 0)),
+    dict(lens=(700, 5, 300), G=32, P=128),
+    dict(lens=(600, 1), G=16, P=256, splits=2),
 ]
 
 
