@@ -458,9 +458,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 } else {
                     const int64_t prow = (int64_t)it * nq * Hq + qr;
                     float *dst = a.ws_o + prow * a.Dv + d0;
-                    *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
-                    *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
-                    if (d0 == 0) a.ws_lse[prow] = lse_v;
+                    if (a.counters) {                 // merged inside this launch
+#pragma unroll
+                        for (int k = 0; k < 8; k++) store_shared(dst + k, o[k]);
+                        if (d0 == 0) store_shared(a.ws_lse + prow, lse_v);
+                    } else {
+                        *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+                        *(f32x4 *)(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+                        if (d0 == 0) a.ws_lse[prow] = lse_v;
+                    }
                 }
             }
         }

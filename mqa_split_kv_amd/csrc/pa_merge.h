@@ -31,7 +31,23 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 // the final reduction adds the sink to the denominator).
 constexpr int kChunkBatch = 4;
 
-template <int kUnits>
+// Partials shared across workgroups inside one launch (the fused combine) are written and
+// read with agent-scope relaxed atomics: on gfx950 such stores and loads are coherent at
+// device scope by themselves (the sc1 cache policy: through the non-coherent per-XCD L2),
+// so ordering them only takes a wait for the stores and the counter atomic, and no fence,
+// i.e. no write-back or invalidation of the whole L2.
+__device__ inline void store_shared(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_shared(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// COHERENT: the partials come from other workgroups of the same launch (read with
+// load_shared); else from an earlier launch (plain loads).
+template <int kUnits, bool COHERENT = false>
 __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const float *sinks,
                                   uint16_t *out, float *lse, int b, int64_t c0, int n, int Hq,
                                   int nq, int Dv, int hq0, int nrows, int tid, int nthr)
@@ -71,9 +87,15 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
                 for (int k = 0; k < kChunkBatch; k++) {
                     const bool in = ok[j] && i0 + k < n;
                     const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hr;
-                    lv[j][k] = in ? ws_lse[prow] : -INFINITY;
-                    ov[j][k] = in ? *(const merge_f32x4 *)(ws_o + prow * Dv + d0)
-                                  : merge_f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (COHERENT) {
+                        lv[j][k] = in ? load_shared(ws_lse + prow) : -INFINITY;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) ov[j][k][e] = in ? load_shared(ws_o + prow * Dv + d0 + e) : 0.f;
+                    } else {
+                        lv[j][k] = in ? ws_lse[prow] : -INFINITY;
+                        ov[j][k] = in ? *(const merge_f32x4 *)(ws_o + prow * Dv + d0)
+                                      : merge_f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
             }
 #pragma unroll
@@ -118,11 +140,12 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
 
 // Fused combine, called by every thread of a workgroup once it has processed all its
 // items [ib, ie) (row group rg: query heads [hq0, hq0 + nrows) of every query token;
-// `arrivals` workgroups write partials per chunk of the row group).  Release: each thread's
-// partial writes are made visible at device scope (one fence per workgroup), then one
-// thread counts each of the workgroup's partial chunks in; the workgroup that counts a
-// request's last chunk acquires the other workgroups' writes, merges that request, and
-// returns its counter to zero.  Then requests with no chunk at all (length 0 under the
+// `arrivals` workgroups write partials per chunk of the row group).  The partials were
+// written with store_shared; each thread waits until its stores are complete, the
+// workgroup meets, and one thread counts each of the workgroup's partial chunks in with a
+// device-scope atomic; the workgroup that counts a request's last chunk reads the other
+// workgroups' partials with load_shared (every store it needs completed before the count
+// it observed), merges that request, and returns its counter to zero.  Then requests with no chunk at all (length 0 under the
 // balanced rule) get out = 0, lse = -inf (or the sink) from workgroup part = b mod
 // num_parts.
 __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *plan, int part,
@@ -130,12 +153,11 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
                                           int nrows, int arrivals, int *s_flag)
 {
     const int Hq = a.Hkv * a.G, nq = a.q_len;
-    // the release (a write-back of the XCD's L2) is only paid by workgroups that wrote
-    // partials: with every request in one chunk the fused path costs nothing
+    // with every request in one chunk the fused path costs nothing
     bool wrote = false;
     for (int it = ib; it < ie; it++) wrote |= !(plan[a.items_off + 4 * it + 3] & 1);
     if (wrote) {
-        __threadfence();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partials are out
         __syncthreads();
     }
     for (int it = ib; it < ie; it++) {
@@ -145,13 +167,12 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
         const int n = plan[a.chunk_off_off + b + 1] - c0;
         int32_t *cnt = a.counters + (int64_t)b * n_rowgroups + rg;
         if (threadIdx.x == 0)
-            *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+            *s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                       n * arrivals - 1;
         __syncthreads();
         if (*s_flag) {
-            __threadfence();
-            merge_rows<4>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
-                          nrows, threadIdx.x, blockDim.x);
+            merge_rows<4, true>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
+                                nrows, threadIdx.x, blockDim.x);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();

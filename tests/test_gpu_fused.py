@@ -17,7 +17,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity, bf16_bits_to_f64
+from gpu_util import GpuRun, assert_parity, bf16_bits_to_f64, to_device
 from test_gpu_decode import _case, _mla_case
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +69,24 @@ def test_fused_repeated_runs_one_plan():
         torch.cuda.synchronize()
         o2, l2 = bf16_bits_to_f64(run.out), run.lse.cpu().numpy().astype(np.float64)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        _check_counters_zero(run)
+
+
+@pytest.mark.parametrize("kw", [dict(Hq=32, Hkv=8, D=128, P=16, lens=(3000, 17, 900, 4096, 0, 65)),
+                                dict(Hq=32, Hkv=4, D=64, P=256, lens=(1536,) * 8, splits=8)])
+def test_fused_changing_inputs_one_workspace(kw):
+    """Runs on one plan and workspace with different q and KV each time: the merging
+    workgroup must see this launch's partials, never an earlier launch's."""
+    cases = [_case(seed=s, **kw) for s in (21, 22, 23)]
+    run = GpuRun(cases[0], fused=True)
+    run.plan()
+    for c in cases + cases[:1]:
+        run.dev = to_device(c)
+        run.step()
+        torch.cuda.synchronize()
+        o, l = bf16_bits_to_f64(run.out), run.lse.cpu().numpy().astype(np.float64)
+        ref_out, ref_lse = oracle.decode(c)
+        assert_parity(c, o, l, ref_out, ref_lse)
         _check_counters_zero(run)
 
 
