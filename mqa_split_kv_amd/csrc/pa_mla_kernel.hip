@@ -67,6 +67,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define PA_LDS __attribute__((address_space(3)))
 
@@ -84,7 +86,6 @@ constexpr int kRawTile = kT * kRawRow;             // 21504
 constexpr int kRawSlots = 6;                       // tile ring
 constexpr int kAhead = kRawSlots - 2;              // lookups: page ids 4, positions 8 tiles ahead
 constexpr int kLookRing = 16;                      // lookup slots (tiles) per wave
-constexpr int kKSteps = kDqk / 32;                 // 18 (k = 32 per MFMA)
 constexpr int kDvBlocks = kDv / 16;                // 32 PV MFMAs per tile and wave
 constexpr float kLazyMax = 8.0f;                   // log2 units
 
@@ -160,6 +161,60 @@ __device__ __forceinline__ float col_sum(float x)
     x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Q as two fp8 terms for the scaled fp8 MFMA: hi = e4m3(v 2^-e_hi), lo = e4m3((v - hi
+// 2^e_hi) 2^-e_lo), with e the power of two that brings the max |.| over the head's 128
+// dims (this lane's 32 and those of lanes l^16, l^32, l^48) into [128, 256), within the
+// E8M0 range.  A bf16 value has 8 significant bits and each term keeps 4, so hi + lo is v
+// exactly for every v within 2^13 of the maximum, and within 2^-21 of it otherwise.
+__device__ __forceinline__ int split_exp(float mx)
+{
+    return max(__builtin_amdgcn_frexp_expf(col_max(mx)) - 8, -127);
+}
+__device__ __forceinline__ int fp8x4_code(const float *v, int e)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[0], -e), __builtin_amdgcn_ldexpf(v[1], -e), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[2], -e), __builtin_amdgcn_ldexpf(v[3], -e), w, true);
+}
+__device__ __forceinline__ int q_split_exp(const float (&v)[32])
+{
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(v[i]));
+    return split_exp(mx);
+}
+__device__ __forceinline__ int q_split_lo(const float (&v)[32], int e_hi, i32x8 &hi, i32x8 &lo)
+{
+    float r[32], mx = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+        const int w = fp8x4_code(&v[4 * d], e_hi);
+        hi[d] = w;
+        const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        r[4 * d + 0] = v[4 * d + 0] - __builtin_amdgcn_ldexpf(x0[0], e_hi);
+        r[4 * d + 1] = v[4 * d + 1] - __builtin_amdgcn_ldexpf(x0[1], e_hi);
+        r[4 * d + 2] = v[4 * d + 2] - __builtin_amdgcn_ldexpf(x1[0], e_hi);
+        r[4 * d + 3] = v[4 * d + 3] - __builtin_amdgcn_ldexpf(x1[1], e_hi);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(r[i]));
+    const int e_lo = split_exp(mx);
+#pragma unroll
+    for (int d = 0; d < 8; d++) lo[d] = fp8x4_code(&r[4 * d], e_lo);
+    return e_lo;
+}
+
+// scaled fp8 MFMA 16x16x128 (both operands e4m3): A unscaled, B scaled by byte u of sc
+__device__ __forceinline__ f32x4 mfma_fp8_q(int u, const i32x8 &a, const i32x8 &b, const f32x4 &c, uint32_t sc)
+{
+    switch (u) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, (int)sc);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 1, (int)sc);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 2, (int)sc);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 3, (int)sc);
+    }
 }
 
 // SPARSE: index-slot items.  MASKED: a per-wave key range narrower than the item (draft
@@ -287,21 +342,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         };
 
-        // ---- Q^T operand of this wave's 16 heads (B of the MFMA), resident, in the k order
-        //      of the code reads: step 2p + h <- dims 64p + 16g4 + 8h .. +7 (p < 8), step
-        //      16 + r <- rope dims 512 + 32r + 8g4 .. +7.  A wave with no query rows runs
-        //      the same instruction stream on a zero Q; it writes nothing.
-        bf16x8 qop[kKSteps];
-        if (active) {
+        // ---- Q^T operand of this wave's 16 heads (B of the MFMAs), resident.  Latent dims:
+        //      for each 128-dim tile u, an fp8 pair q = hi 2^e_hi + lo 2^e_lo (power-of-two
+        //      scales per head and tile, taken by the scaled MFMA), so the K codes enter the
+        //      MFMA as they are; lane (col, g4) holds dims 128u + 16g4 + 0..15 (bytes 0-15)
+        //      and 128u + 64 + 16g4 + 0..15 (bytes 16-31), the k order of the fp8 MFMA.  Rope
+        //      dims stay bf16: step r <- dims 512 + 32r + 8g4 .. +7.  A wave with no query
+        //      rows runs the same instruction stream on a zero Q; it writes nothing.
+        i32x8 qhi[4], qlo[4];
+        uint32_t qsc_hi = 0x7F7F7F7Fu, qsc_lo = 0x7F7F7F7Fu;   // E8M0 byte u: tile u
+        bf16x8 qrope[2];
+        {
             const uint16_t *qrow = a.q + (((int64_t)b * nq + qi) * Hq + head0 + col) * kDqk;
 #pragma unroll
-            for (int s = 0; s < kKSteps; s++) {
-                const int d = s < 16 ? 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : 512 + 32 * (s - 16) + 8 * g4;
-                qop[s] = *(const bf16x8 *)(qrow + d);
-            }
-        } else {
+            for (int u = 0; u < 4; u++) {
+                float v[32];
+                u32x4 raw4[4];
 #pragma unroll
-            for (int s = 0; s < kKSteps; s++) qop[s] = bf16x8{};
+                for (int h = 0; h < 4; h++)
+                    raw4[h] = active ? *(const u32x4 *)(qrow + 128 * u + 64 * (h >> 1) + 16 * g4 + 8 * (h & 1))
+                                     : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const uint32_t w2 = raw4[i >> 2][i & 3];
+                    v[2 * i] = __uint_as_float(w2 << 16);
+                    v[2 * i + 1] = __uint_as_float(w2 & 0xFFFF0000u);
+                }
+                const int e_hi = q_split_exp(v);
+                const int e_lo = q_split_lo(v, e_hi, qhi[u], qlo[u]);
+                qsc_hi = (qsc_hi & ~(0xFFu << (8 * u))) | ((uint32_t)(127 + e_hi) << (8 * u));
+                qsc_lo = (qsc_lo & ~(0xFFu << (8 * u))) | ((uint32_t)(127 + e_lo) << (8 * u));
+            }
+#pragma unroll
+            for (int r = 0; r < 2; r++)
+                qrope[r] = active ? *(const bf16x8 *)(qrow + 512 + 32 * r + 8 * g4) : bf16x8{};
         }
 
         f32x4 acc[kDvBlocks];
@@ -311,9 +385,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         float l = 0.f;
 
         // ---- S^T of tile t (rows: this lane's tokens 8g4 + 4sb + r, r = 0..3): one partial
-        //      per 128-dim scale tile (k-steps 4t'..4t'+3) and one for the rope dims
-        //      (k-steps 16, 17), combined with the token scales in fp32.  inter(k) runs
-        //      right after MFMA k (k = 0..35), with nothing moved across it.
+        //      per 128-dim scale tile (two scaled fp8 MFMAs 16x16x128: Q's hi and lo terms)
+        //      and one for the rope dims (two bf16 MFMAs 16x16x32), combined with the token
+        //      scales in fp32.  inter(k) runs right after MFMA slot k (k = 0..19), with
+        //      nothing moved across it.
         auto qk_tile = [&](int t, float (&st)[8], auto &&inter) {
             const uint8_t *slot = raw[t % kRawSlots];
 #pragma unroll
@@ -322,32 +397,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                 for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                 const uint8_t *kbase = slot + qk_off0 + 4 * sb * kRawRow;
-                // read q < 8: 16 bytes of codes (k-steps 2q, 2q+1); q = 8, 9: 16 bytes of
-                // rope (k-step 8 + q)
-                auto rd = [&](int q) {
-                    return *(const u32x4 *)(kbase + (q < 8 ? 64 * q : 528 + 64 * (q - 8)));
+                // the 32 code bytes of tile u in the fp8 MFMA's k order
+                auto rd_codes = [&](int u) {
+                    const u32x4 x = *(const u32x4 *)(kbase + 128 * u);
+                    const u32x4 y = *(const u32x4 *)(kbase + 128 * u + 64);
+                    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
                 };
-                // the A operand of k-step ks from read q = ks / 2 (ks < 16) or ks - 8
-                auto kop_of = [](int ks, const u32x4 &v) {
-                    if (ks >= 16) return __builtin_bit_cast(bf16x8, v);
-                    return (ks & 1) ? fp8x8_to_bf16(v[2], v[3]) : fp8x8_to_bf16(v[0], v[1]);
-                };
-                auto q_of = [](int ks) { return ks < 16 ? ks >> 1 : ks - 8; };
-                u32x4 w[3];
-                w[0] = rd(0);
-                w[1] = rd(1);
-                // operands are converted one MFMA ahead (no VALU-to-MFMA wait states)
-                bf16x8 kop[2];
-                kop[0] = kop_of(0, w[0]);
+                auto rd_rope = [&](int r) { return *(const bf16x8 *)(kbase + 512 + 16 + 64 * r); };
+                i32x8 kc[4];
+                bf16x8 kr[2];
+                kc[0] = rd_codes(0);
+                kc[1] = rd_codes(1);
+                // slot k: tiles (0, 1) hi, (0, 1) lo, (2, 3) hi, (2, 3) lo, rope 0, 1; each
+                // read is issued two slots or more before its first use
 #pragma unroll
-                for (int ks = 0; ks < kKSteps; ks++) {
-                    const int q = q_of(ks);
-                    const bool first = ks < 16 ? (ks & 1) == 0 : true;
-                    if (first && q + 2 < 10) w[(q + 2) % 3] = rd(q + 2);
-                    const int p = ks < 16 ? ks / 4 : 4;
-                    part[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks & 1], qop[ks], part[p], 0, 0, 0);
-                    if (ks + 1 < kKSteps) kop[(ks + 1) & 1] = kop_of(ks + 1, w[q_of(ks + 1) % 3]);
-                    inter(kKSteps * sb + ks);
+                for (int k = 0; k < 10; k++) {
+                    if (k == 0) kc[2] = rd_codes(2);
+                    if (k == 1) kc[3] = rd_codes(3);
+                    if (k == 4) kr[0] = rd_rope(0);
+                    if (k == 5) kr[1] = rd_rope(1);
+                    if (k < 8) {
+                        const int u = 2 * (k >> 2) + (k & 1);
+                        const bool lo = (k & 2) != 0;
+                        part[u] = mfma_fp8_q(u, kc[u], lo ? qlo[u] : qhi[u], part[u], lo ? qsc_lo : qsc_hi);
+                    } else {
+                        part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k - 8], qrope[k - 8], part[4], 0, 0, 0);
+                    }
+                    inter(10 * sb + k);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll

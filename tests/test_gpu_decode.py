@@ -289,6 +289,28 @@ def test_mla_config_full_sampled():
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
 
 
+def test_mla_q_dynamic_range():
+    """Query rows whose 128-dim latent tiles span many binades, with outliers, tiny values,
+    zeros, an all-zero tile and an all-zero head: the kernel's split of the bf16 query
+    into two scaled fp8 terms must still give the oracle's result."""
+    case = _mla_case(lens=(700, 64, 1), G=32, P=64)
+    B, Hq = case["B"], case["Hkv"] * case["G"]
+    rng = np.random.default_rng(5)
+    q = (case["q"].astype(np.uint32) << 16).view(np.float32).reshape(B, Hq, 576).astype(np.float64)
+    q *= 2.0 ** rng.integers(-10, 3, size=(B, Hq, 1))
+    q[..., :512] *= np.repeat(2.0 ** rng.integers(-4, 3, size=(B, Hq, 4)), 128, axis=-1)
+    u = rng.random(q.shape)
+    q[u < 0.01] *= 16.0
+    q[(u >= 0.01) & (u < 0.06)] *= 2.0 ** -18
+    q[(u >= 0.06) & (u < 0.11)] = 0.0
+    q[0, 3] = 0.0
+    q[1, 5, 256:384] = 0.0
+    case["q"] = synth.f32_to_bf16_bits(q.astype(np.float32)).reshape(case["q"].shape)
+    out, lse = GpuRun(case)()
+    ref_out, ref_lse = oracle.decode(case)
+    assert_parity(case, out, lse, ref_out, ref_lse)
+
+
 @pytest.mark.parametrize("splits", [0, 1])
 def test_mla_needle(splits):
     lens = (257, 96)
