@@ -241,12 +241,13 @@ __device__ __forceinline__ f32x4 mfma_fp8_q(int u, const i32x8 &a, const i32x8 &
 // builtin the compiler may rename O^T's blocks from one tile to the next and copy them
 // back at the loop edge, 4 cycles per register), and they are ordinary VGPRs: one
 // kernel has one split between VGPRs and accumulation registers, and the score waves'
-// registers are VGPRs.  The compiler does not see into the asm,
-// so the operand wait states after the VALU writes of A and B are in it, and every VALU
-// read of O^T after the last of these MFMAs follows mfma_acc_drain().
+// registers are VGPRs.  The compiler does not see into the asm: a VALU write of A, B or
+// the accumulator must be at least 2 instructions before it (the callers convert A two
+// MFMAs ahead), and every VALU read of O^T after the last of these MFMAs follows
+// mfma_acc_drain().
 __device__ __forceinline__ void mfma_acc(f32x4 &acc, const bf16x8 &a, const bf16x8 &b)
 {
-    asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // The drain waits out the MFMA latency and redefines every accumulator through the asm,
 // so no read of O^T can be placed above it.
@@ -272,9 +273,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 {
     constexpr int kLoadsPerTile = MlaCfg<SPARSE>::kLoadsPerTile;
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
-    // probabilities of a tile from the score wave of head block hg, in its lanes' layout
-    // (lane (col, g4): head col, tokens 8g4 + 0..7): [tile parity][hg][tokens 0-3 | 4-7][lane]
-    __shared__ f32x4 s_p[2][4][2][64];
+    // the PV B operands of a tile from the score wave of head block hg, in its lanes' layout
+    // (lane (col, g4): head col, tokens 8g4 + 0..7): P^T times value tile t's token scales,
+    // bf16: [tile parity][hg][value tile t][lane]
+    __shared__ bf16x8 s_p[2][4][4][64];
     __shared__ float s_alpha[2][4][16];       // factor on O^T before the tile's PV, per head
     __shared__ float s_inv[4][16];            // the item's final 1 / l, per head
     __shared__ __attribute__((aligned(4))) uint8_t s_valid[kRawSlots][kWaves];   // sparse: real-token bits
@@ -366,6 +368,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             return pg;
         };
 
+        // ---- dense loads of tile t: the wave's 4 tokens are consecutive slots of one page;
+        //      dn_prep makes their first address, dn_part(k) loads token k (k < 4) or the page
+        //      id of tile t + kAhead (k = 4).  In the tile loop each wave puts its parts
+        //      between its MFMAs: issued at once after the barrier, the 8 waves' loads would
+        //      queue behind each other at the CU's memory port.
+        const uint8_t *d_tok = a.k_pool;
+        int d_nreal = 0, d_t = 0;
+        uint32_t d_lds0 = 0;
+        auto dn_prep = [&](int t, int page) {
+            const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 4 tokens
+            d_tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
+            d_nreal = min(max(t1 - tw, 0), kTokPerWave);
+            d_lds0 = lds_addr(&raw[t % kRawSlots][kTokPerWave * wave * kRawRow]);
+            d_t = t;
+        };
+        auto dn_part = [&](int k) {
+            if (k < kTokPerWave) {
+                if (lane < kChunks)
+                    lds_dma_buf16(d_tok + (int64_t)k * a.s_tok_b, k < d_nreal ? kTokBytes : 0, 16 * lane, d_lds0 + k * kRawRow);
+            } else {
+                dn_issue_page(d_t + kAhead);
+            }
+        };
+        auto dn_rest = [&]() {                     // all parts (a role with no MFMAs this tile)
+#pragma unroll
+            for (int k = 0; k <= kTokPerWave; k++) dn_part(k);
+        };
+
         // ---- loads of tile t into its ring slot: token tt of the wave (tile row 4 wave + tt)
         //      by lanes 0-40 through a buffer over that token's 656 bytes, or over none (reads
         //      as zeros) when it is not real.  Sparse: the page ids of tile t + kAhead and the
@@ -391,28 +421,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 if (lane == 0) s_valid[t % kRawSlots][wave] = (uint8_t)vm;
             } else {
-                const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 4 tokens
-                const uint8_t *tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
-                const int nreal = min(max(t1 - tw, 0), kTokPerWave);
-                const uint32_t lds0 = lds_addr(dst);
+                dn_prep(t, page);
 #pragma unroll
-                for (int tt = 0; tt < kTokPerWave; tt++)
-                    if (lane < kChunks)
-                        lds_dma_buf16(tok + (int64_t)tt * a.s_tok_b, tt < nreal ? kTokBytes : 0, 16 * lane, lds0 + tt * kRawRow);
-                dn_issue_page(t + kAhead);
+                for (int k = 0; k <= kTokPerWave; k++) dn_part(k);
             }
         };
 
         // ---- top of tile i (both roles, same barriers): tile i's loads in (tiles i+1 ..
         //      i+kAhead-1 are younger), all waves past tile i-1 (slot of tile i-2 free, the
-        //      probabilities of tile i-1 stored), then tile i+kAhead's loads into its slot
+        //      B operands of tile i-1 stored), then tile i+kAhead's loads into its slot
+        //      (dense: prepared here, issued by the role between its MFMAs; every wave issues
+        //      exactly one tile's loads per iteration, which the wait counts rely on)
         auto tile_top = [&](int i) {
             wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
             if (SPARSE) {
                 lds_barrier();
                 issue_tile(i + kAhead, 0);
             } else {
-                issue_tile(i + kAhead, page_barrier(i + kAhead));
+                dn_prep(i + kAhead, page_barrier(i + kAhead));
             }
         };
 
@@ -477,7 +503,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
             for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                 tile_top(i);
-                if (i == ntiles) break;
+                if (i == ntiles) {
+                    if (!SPARSE) dn_rest();
+                    break;
+                }
                 PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[i % kRawSlots];
                 // ---- S^T of tile i (rows: this lane's tokens 8g4 + 4sb + r): one partial per
                 //      128-dim scale tile u (two scaled fp8 MFMAs 16x16x128, Q's hi and lo
@@ -493,20 +522,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 };
                 auto rd_rope = [&](int sb, int r) { return *(PA_LDS const bf16x8 *)(slot + rope_off + 4 * sb * kRawRow + 64 * r); };
                 float st[8];
+                f32x4 sc_tok[8];                   // token 8g4 + r's four tile scales
                 i32x8 kc[2][4];
                 bf16x8 kr[2][2];
+                f32x4 part[2][5];
                 kc[0][0] = rd_codes(0, 0);
                 kc[0][1] = rd_codes(0, 1);
+                // row r of row block sb: the token scales times the tile partials, plus rope
+                auto combine = [&](int sb, int r) {
+                    float x = part[sb][4][r];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) x += sc_tok[4 * sb + r][u] * part[sb][u][r];
+                    st[4 * sb + r] = x;
+                };
 #pragma unroll
                 for (int sb = 0; sb < 2; sb++) {
-                    f32x4 part[5];
 #pragma unroll
-                    for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int p = 0; p < 5; p++) part[sb][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k = 0; k < 10; k++) {
-                        // reads issued at this slot
+                        // reads issued at this slot (the token scales early, for the combine)
                         if (k == 0) kc[sb][2] = rd_codes(sb, 2);
                         if (k == 1) kc[sb][3] = rd_codes(sb, 3);
+                        if (k >= 2 && k < 6)
+                            sc_tok[4 * sb + k - 2] = *(PA_LDS const f32x4 *)(slot + sc_off + (4 * sb + k - 2) * kRawRow);
                         if (k == 6) kr[sb][0] = rd_rope(sb, 0);
                         if (k == 7) kr[sb][1] = rd_rope(sb, 1);
                         if (sb == 0 && k == 8) kc[1][0] = rd_codes(1, 0);
@@ -514,21 +553,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         if (k < 8) {
                             const int u = 2 * (k >> 2) + (k & 1);
                             const bool lo = (k & 2) != 0;
-                            part[u] = mfma_fp8_q(u, kc[sb][u], lo ? qlo[u] : qhi[u], part[u], lo ? qsc_lo : qsc_hi);
+                            part[sb][u] = mfma_fp8_q(u, kc[sb][u], lo ? qlo[u] : qhi[u], part[sb][u], lo ? qsc_lo : qsc_hi);
                         } else {
-                            part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k - 8], qrope[k - 8], part[4], 0, 0, 0);
+                            part[sb][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k - 8], qrope[k - 8], part[sb][4], 0, 0, 0);
                         }
+                        // row block 0's combine runs under row block 1's MFMAs
+                        if (sb == 1 && k >= 1 && k < 5) combine(0, k - 1);
+                        if (!SPARSE && sb == 0 && k <= kTokPerWave) dn_part(k);
                         __builtin_amdgcn_sched_barrier(0);
                     }
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const f32x4 sc = *(PA_LDS const f32x4 *)(slot + sc_off + (4 * sb + r) * kRawRow);
-                        float x = part[4][r];
-#pragma unroll
-                        for (int u = 0; u < 4; u++) x += sc[u] * part[u][r];
-                        st[4 * sb + r] = x;
-                    }
                 }
+#pragma unroll
+                for (int r = 0; r < 4; r++) combine(1, r);
                 // ---- softmax: logits and mask, the max over the head's 32 tokens, the
                 //      lazily moved reference, p = 2^(s - m) and the row sum; P and the factor
                 //      for O^T (1 unless the reference moved) go to the value wave
@@ -558,8 +594,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 l = l * alpha + ps;
                 m = m_new;
-                s_p[i & 1][hg][0][lane] = f32x4{pr[0], pr[1], pr[2], pr[3]};
-                s_p[i & 1][hg][1][lane] = f32x4{pr[4], pr[5], pr[6], pr[7]};
+                // the value wave's B operands: P^T times each value tile's token scales (the
+                // value is the key's first 512 dims, so the scales are the key tile scales)
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    bf16x8 pb;
+#pragma unroll
+                    for (int r = 0; r < 8; r++) pb[r] = (__bf16)(pr[r] * sc_tok[r][t]);
+                    s_p[i & 1][hg][t][lane] = pb;
+                }
                 if (g4 == 0) s_alpha[i & 1][hg][col] = alpha;
             }
 
@@ -611,44 +654,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                 tile_top(i);
                 if (i == 0) {
+                    if (!SPARSE) dn_rest();
                     PA_LDS uint8_t *vb0 = vbase(0);
 #pragma unroll
                     for (int d = 0; d < kVPre; d++) vw[d] = rd(vb0, d);
                     continue;
                 }
                 const int j = i - 1;
-                PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[j % kRawSlots];
                 PA_LDS uint8_t *vb = vbase(j);
-                // the tile's factor for O^T, probabilities and token scales, read together
+                // the tile's factor for O^T and the B operands (P^T times value tile t's token
+                // scales, from the score wave), read together
                 const float alpha = s_alpha[j & 1][hg][col];
-                const f32x4 p0 = s_p[j & 1][hg][0][lane], p1 = s_p[j & 1][hg][1][lane];
-                f32x4 sc[8];
+                bf16x8 pbt[4];
 #pragma unroll
-                for (int r = 0; r < 8; r++) sc[r] = *(PA_LDS const f32x4 *)(slot + sc_off + r * kRawRow);
+                for (int t = 0; t < 4; t++) pbt[t] = s_p[j & 1][hg][t][lane];
                 if (__any(alpha != 1.f)) {                   // rare: the reference moved
                     mfma_acc_drain(acc);
 #pragma unroll
                     for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha;
                 }
-                const float pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-                // B = P^T times the value tile's token scales (pbt[t] for value tile t)
-                bf16x8 pbt[4];
-#pragma unroll
-                for (int r = 0; r < 8; r++) {
-#pragma unroll
-                    for (int t = 0; t < 4; t++) pbt[t][r] = (__bf16)(pr[r] * sc[r][t]);
-                }
-                // A = V^T converted to bf16 one MFMA ahead
-                bf16x8 va[2];
+                // A = V^T converted to bf16 two MFMAs ahead (no wait states before the MFMA)
+                bf16x8 va[3];
                 va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
+                va[1] = fp8x8_to_bf16((uint32_t)vw[1][0], (uint32_t)vw[1][1]);
 #pragma unroll
                 for (int db = 0; db < kDvBlocks; db++) {
                     if (db + kVPre < kDvBlocks) vw[(db + kVPre) % kVRing] = rd(vb, db + kVPre);
-                    mfma_acc(acc[db], va[db & 1], pbt[db >> 3]);
-                    if (db + 1 < kDvBlocks) {
-                        const i32x2 w = vw[(db + 1) % kVRing];
-                        va[(db + 1) & 1] = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+                    mfma_acc(acc[db], va[db % 3], pbt[db >> 3]);
+                    if (db + 2 < kDvBlocks) {
+                        const i32x2 w = vw[(db + 2) % kVRing];
+                        va[(db + 2) % 3] = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
                     }
+                    if (!SPARSE && (db & 3) == 0 && db / 4 <= kTokPerWave) dn_part(db / 4);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i < ntiles) {
