@@ -7,18 +7,21 @@
 //
 // One workgroup (8 waves, two per SIMD) = one (part, group of 64 query rows); it walks
 // the part's items.  Query rows are (draft token qi, head g) pairs, row qi * G + g, so with
-// several query tokens per request (a linear speculative draft) each wave pair's 16 rows
-// share one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a
+// several query tokens per request (a linear speculative draft) each block of 16 rows
+// shares one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a
 // part run as workgroups 8 ids apart, i.e. on the same XCD at about the same time, so the
 // second read of each KV tile is an L2 hit (the FlashMLA walk-through shares one KV tile
 // between two 64-head CTAs through a cluster, section 计算环节一; here the L2 of the XCD
 // plays that role).
 //
-// Wave w = (hg, kh) = (w % 4, w / 4): the pair with the same hg owns 16 query heads and
-// sits on one SIMD.  Each member computes half of the scores' contraction (the latent dims
-// of its two 128-dim scale tiles 2kh, 2kh+1 and half of the rope dims) and half of the
-// output (value dims 256kh .. 256kh+255); the two partial scores meet through LDS.  Two
-// waves per SIMD let one wave's conversions, softmax and waits run under the other's
+// Waves hg and hg + 4 share a SIMD and one block of 16 query heads, with two roles (the
+// FlashMLA walk-through splits a tile's work over two warpgroups, section 计算环节二; here
+// the split is by operation):
+//   * the score wave (Q resident) computes S^T[32 tok x 16 heads] = K . Q^T of tile i and
+//     its softmax in iteration i, and hands the PV operands to the value wave through LDS;
+//   * the value wave (O^T[512 x 16 heads] resident) runs O^T += V^T . P^T of tile i-1 in
+//     iteration i.
+// Two waves per SIMD let one wave's conversions, softmax and waits run under the other's
 // matrix work, which one wave cannot do for itself (a wave's dependent VALU chains and its
 // LDS and barrier waits stall its own MFMA issue).
 //
@@ -26,38 +29,34 @@
 //   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
 //     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 5-slot
 //     ring of 752-byte rows (the stride at which both operand read patterns below run at
-//     the LDS's measured best), so each tile's loads are issued 4 tiles ahead.  Page ids
-//     come the same way, 3 tiles ahead, into a small LDS ring (a scalar load would make
-//     every later LDS wait also wait for it);
-//   * scores: S^T[32 tok x 16 heads] = K . Q^T.  The FP8 codes enter a scaled fp8 MFMA
-//     16x16x128 as they are; Q is resident as two e4m3 terms with power-of-two scales per
-//     head and tile (q = hi 2^e_hi + lo 2^e_lo, exact to 2^-21 of the tile's max), so each
-//     128-dim tile is two MFMAs.  The rope dims use bf16 MFMA 16x16x32.  The token scales
-//     are applied in fp32 to the per-tile partials: S = sum_t scale_t (q_t . k_t) + q_rope .
-//     k_rope.  (The FlashMLA walk-through dequantises to bf16 and runs bf16 MMA with fp32
-//     accumulation, section 计算环节一; here no operand of the score product is converted.)
-//   * an online softmax per head column, duplicated in both waves of the pair on the same
-//     summed scores, so both hold the same reference max, probabilities and row sum;
-//   * O^T[256 x 16 heads] += V^T . P^T with bf16 MFMA 16x16x32, V^T read transposed from
-//     the FP8 codes (ds_read_b64_tr_b8) and converted in registers (exact); the
-//     probabilities are multiplied by the value tile's token scales before the MFMA.  O^T
-//     lives in 64 accumulation registers (the register-budget problem the FlashMLA
-//     walk-through describes in section 计算环节二, solved here by splitting the value dims
-//     over the pair).
+//     the LDS's measured best); tile i+3's loads go out in iteration i, each wave putting
+//     its own between its MFMAs.  Page ids come the same way, 3 tiles ahead, into a small
+//     LDS ring (a scalar load would make every later LDS wait also wait for it);
+//   * scores: the FP8 codes enter a scaled fp8 MFMA 16x16x128 as they are; Q is resident as
+//     two e4m3 terms with power-of-two scales per head and tile (q = hi 2^e_hi + lo 2^e_lo,
+//     exact to 2^-21 of the tile's max), so each 128-dim tile is two MFMAs.  The rope dims
+//     use bf16 MFMA 16x16x32.  The token scales are applied in fp32 to the per-tile
+//     partials: S = sum_t scale_t (q_t . k_t) + q_rope . k_rope.  (The FlashMLA walk-through
+//     dequantises to bf16 and runs bf16 MMA with fp32 accumulation, section 计算环节一; here
+//     no operand of the score product is converted.)
+//   * an online softmax per head column; the score wave writes P^T times each 128-dim value
+//     tile's token scales (bf16, the B operands of the PV MFMAs) and the factor for O^T (1
+//     unless the reference max moved);
+//   * O^T += V^T . P^T with bf16 MFMA 16x16x32, V^T read transposed from the FP8 codes
+//     (ds_read_b64_tr_b8) and converted in registers (exact).  O^T takes 128 registers (the
+//     register-budget problem the FlashMLA walk-through describes in section 计算环节二),
+//     ordinary VGPRs: one kernel has one split between VGPRs and accumulation registers,
+//     and the score wave's registers are VGPRs.
 // Operand layouts.  QK row block sb (0, 1) of the A operand holds, in MFMA row m = 4g + r,
 // token 8g + 4sb + r, so lane group g of the S^T result holds tokens 8g..8g+7: exactly the
-// k slots the same lanes feed to the PV MFMA (B = P^T, k = 8g + j), and the transposed
-// read returns tokens 8g..8g+7 of one value dim per lane.  In the fp8 MFMA lane (col, g)
-// holds dims 16g + 0..15 and 64 + 16g + 0..15 of the 128-dim tile.
-// The tile loop is software-pipelined:
-//   top of tile j: the loads of tile j+1 are in; workgroup barrier (also publishes the
-//   partial scores of tile j);
-//   phase 1: the QK MFMAs of tile j+1 (partial), with the softmax of tile j between them;
-//            the partial scores of tile j+1 go to LDS;
-//   phase 2: the PV MFMAs of tile j, with the loads of tile j+4 between them.
-// The running max is only moved when a tile's max exceeds it by more than 2^8, so the
-// rescale is rare; probabilities stay below 2^8 and the result is the same up to rounding
-// (the reference cancels in the final normalisation).
+// k slots the same lanes of the value wave feed to the PV MFMA (B = P^T, k = 8g + j), and
+// the transposed read returns tokens 8g..8g+7 of one value dim per lane; the PV operands
+// pass through LDS lane for lane.  In the fp8 MFMA lane (col, g) holds dims 16g + 0..15
+// and 64 + 16g + 0..15 of the 128-dim tile.
+// One workgroup barrier per tile: it publishes the PV operands of tile i-1 and frees the
+// ring slot of tile i-2.  The running max is only moved when a tile's max exceeds it by
+// more than 2^8, so the rescale of O^T is rare; probabilities stay below 2^8 and the result
+// is the same up to rounding (the reference cancels in the final normalisation).
 //
 // Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
 // indices): the items then cover index slots, and slot k of request b names the key
