@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-graph", action="store_true", help="skip timing a hipGraph replay of the step")
+    ap.add_argument("--no-protocol", action="store_true",
+                    help="skip the grouped timing (10 groups of 100 calls, median of group means)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip measuring the HBM read ceiling of the box")
     ap.add_argument("--cold-copies", type=int, default=-1,
                     help="also time with each step reading the next of N copies of the KV pool "
                          "(so that the pool is not cache-resident); -1: automatic (enough copies "
@@ -159,6 +163,29 @@ def main():
     runner.combine(out, lse)
     torch.cuda.synchronize()
 
+    # grouped timing (the MetaX page's protocol: 10 groups of 100 calls after the warm-ups,
+    # median of the group means), eager here and from graphs below
+    groups, calls = 10, 100
+
+    def median_of_groups(one_group):
+        means = []
+        for _ in range(groups):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            one_group()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            means.append(a0.elapsed_time(a1) * 1000.0 / calls)
+        return round(float(np.median(means)), 2)
+
+    proto = None
+    if not args.no_protocol:
+        def eager_group():
+            for _ in range(calls):
+                step()
+        proto = {"groups": groups, "calls_per_group": calls, "eager_us_median": median_of_groups(eager_group),
+                 "graph_us_median": None}
+
     graph_us = decode_graph_us = None
     if not args.no_graph:
         # several steps per graph, so that the per-replay launch cost is amortised and
@@ -185,6 +212,11 @@ def main():
         g1.record()
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1000.0 / (reps * per_graph)
+        if proto is not None:
+            def graph_group():
+                for _ in range(calls // per_graph):
+                    g.replay()
+            proto["graph_us_median"] = median_of_groups(graph_group)
         # the decode kernel alone, launched from a graph: its device time without the host's
         # per-launch cost (which is what eager back-to-back launches of a small kernel time)
         gd = torch.cuda.CUDAGraph()
@@ -241,6 +273,16 @@ def main():
                           + (", eager launches" if decode_graph_us is None else ", graph of launches")}
     roof["algorithmic_bytes"] = kv_bytes
 
+    ceiling = None
+    if not args.no_read_ceiling:
+        try:
+            from mqa_split_kv_amd import probe
+            ceiling = probe.read_ceiling(gib=1.0, reps=3, grids=(2048, 4096))["best_gbs"]
+        except RuntimeError as e:                   # the probe library is not built
+            print(f"[bench] read ceiling not measured: {e}", file=sys.stderr)
+    if ceiling and roof["bound"] == "hbm":
+        roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceiling, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -277,6 +319,8 @@ def main():
         "roofline": roof,
         "cold": None if cold is None else dict(cold, kv_gbs_step=round(kv_bytes / (cold["us_per_step"] * 1e-6) / 1e9, 1),
                                                pct_of_hbm_peak_step=round(100.0 * kv_bytes / (cold["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)),
+        "timing_protocol": proto,
+        "read_ceiling_gbs": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -405,7 +449,18 @@ def cpu_baseline(case, seconds):
             "sample": f"{done_pairs} of {B * Hkv} (request, KV head) pairs, {done_tokens} tokens, "
                       f"{reps} run(s), {spent:.2f} s each; full step extrapolates to "
                       f"{full_us / 1e6:.2f} s",
-            "us_per_step_extrapolated": round(full_us, 1)}
+            "us_per_step_extrapolated": round(full_us, 1), "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
