@@ -2,7 +2,9 @@
 //  * pa_probe_read: streams a buffer once with 16-byte loads and folds it into one
 //    word per workgroup - the HBM read ceiling the decode kernel is compared with;
 //  * pa_probe_copy: plain 16-byte vector copy of a known size - the reference whose
-//    FETCH_SIZE / WRITE_SIZE counter readings calibrate the decode kernel's.
+//    FETCH_SIZE / WRITE_SIZE counter readings calibrate the decode kernel's;
+//  * pa_probe_gather: reads a buffer once as fixed-size chunks in a given order (a page
+//    gather: one chunk = one page of one KV head) - the read ceiling of that pattern.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -47,6 +49,26 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4 *__res
     for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// workgroup w reads chunks order[w * per_wg .. + per_wg) (chunk bytes a multiple of 16)
+__global__ __launch_bounds__(kThreads) void probe_gather_kernel(const uint8_t *__restrict__ src,
+                                                                const int32_t *__restrict__ order,
+                                                                int nchunks, int chunk, int per_wg,
+                                                                uint32_t *__restrict__ sink)
+{
+    uint32_t acc = 0;
+    const int c0 = blockIdx.x * per_wg;
+    const int c1 = min(c0 + per_wg, nchunks);
+    for (int c = c0; c < c1; c++) {
+        const u32x4 *p = (const u32x4 *)(src + (size_t)order[c] * chunk);
+        for (int i = threadIdx.x; i < chunk / 16; i += kThreads) {
+            const u32x4 v = __builtin_nontemporal_load(p + i);
+            acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+        }
+    }
+    // no reduction (a workgroup reads only a few KB); the store keeps the loads live
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +88,20 @@ int pa_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *st
         return 1;
     hipLaunchKernelGGL(probe_copy_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// order: nchunks chunk indices, each < nchunks (a permutation); chunk * nchunks <= bytes
+// of src; sink holds ceil(nchunks / per_wg) words.
+int pa_probe_gather(const void *src, const int32_t *order, int nchunks, int chunk, int per_wg,
+                    uint32_t *sink, void *stream)
+{
+    if (!src || !order || !sink || nchunks <= 0 || chunk <= 0 || (chunk & 15) || per_wg <= 0 ||
+        ((uintptr_t)src & 15))
+        return 1;
+    const int blocks = (nchunks + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL(probe_gather_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const uint8_t *)src, order, nchunks, chunk, per_wg, sink);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

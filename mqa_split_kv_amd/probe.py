@@ -6,6 +6,8 @@ read : streams a fresh buffer once per launch (nontemporal 16-byte loads) and re
        the best GB/s over a few grid sizes - the practical read ceiling of the HBM.
 copy : a plain 16-byte copy of a known size, launched on its own so that rocprofv3
        FETCH_SIZE / WRITE_SIZE readings of it calibrate the decode kernel's.
+gather: reads a buffer once as fixed-size chunks in a random order (a page gather; one
+       chunk = one page of one KV head) - the read ceiling of that access pattern.
 """
 from __future__ import annotations
 
@@ -26,6 +28,8 @@ def _lib():
                                 ctypes.c_void_p]
     L.pa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                 ctypes.c_void_p]
+    L.pa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
@@ -59,6 +63,39 @@ def read_ceiling(gib: float = 2.0, reps: int = 5, grids=(1024, 2048, 4096, 8192)
             "by_grid": {str(k): round(v, 1) for k, v in best.items()}}
 
 
+def gather_ceiling(gib: float = 2.0, chunks=(2048, 16384), reps: int = 4, per_wg=(4, 16, 64)) -> dict:
+    """Best GB/s reading `gib` GiB once as `chunk`-byte pieces in a seeded random order."""
+    import torch
+
+    L = _lib()
+    nbytes = int(gib * (1 << 30)) // 65536 * 65536
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for b in bufs:
+        b.fill_(1)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    res = {}
+    for chunk in chunks:
+        n = nbytes // chunk
+        order = torch.randperm(n, generator=gen).to(torch.int32).cuda()
+        sink = torch.empty(n, dtype=torch.int32, device="cuda")
+        best = 0.0
+        for pw in per_wg:
+            assert L.pa_probe_gather(ctypes.c_void_p(bufs[0].data_ptr()), ctypes.c_void_p(order.data_ptr()),
+                                     n, chunk, pw, ctypes.c_void_p(sink.data_ptr()), stream) == 0
+            torch.cuda.synchronize()
+            for r in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                L.pa_probe_gather(ctypes.c_void_p(bufs[r % 2].data_ptr()), ctypes.c_void_p(order.data_ptr()),
+                                  n, chunk, pw, ctypes.c_void_p(sink.data_ptr()), stream)
+                e1.record()
+                torch.cuda.synchronize()
+                best = max(best, n * chunk / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        res[str(chunk)] = round(best, 1)
+    return res
+
+
 def copy_once(mib: int = 512, blocks: int = 2048) -> dict:
     import torch
 
@@ -87,4 +124,5 @@ if __name__ == "__main__":
     res = {"copy": copy_once(a.copy_mib)}
     if not a.copy_only:
         res["read"] = read_ceiling(a.gib)
+        res["gather_random"] = gather_ceiling(a.gib)
     print(json.dumps(res), flush=True)
