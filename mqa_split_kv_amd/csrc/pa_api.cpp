@@ -259,6 +259,7 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
     a.part_begin_off = L.part_begin_off;
     a.items_off = L.items_off;
     a.chunk_off_off = L.chunk_off_off;
+    a.fixed_splits = desc->num_splits > 0 ? desc->num_splits : 0;
     a.counters = (desc->flags & PA_FLAG_FUSED_COMBINE) && desc->num_splits != 1
                      ? (int32_t *)plan + L.counters_off
                      : nullptr;
@@ -292,7 +293,7 @@ pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const 
                                                          desc->Dv));
     if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, sinks, (uint16_t *)out, lse, desc->B,
                            desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
-                           (hipStream_t)stream) != hipSuccess)
+                           desc->num_splits > 0 ? desc->num_splits : 0, (hipStream_t)stream) != hipSuccess)
         return PA_ERR_DEVICE;
     return PA_OK;
 }

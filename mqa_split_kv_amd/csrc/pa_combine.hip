@@ -12,12 +12,13 @@ constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void pa_combine_kernel(
     const int32_t *__restrict__ plan, const float *__restrict__ ws_o,
     const float *__restrict__ ws_lse, const float *__restrict__ sinks, uint16_t *__restrict__ out,
-    float *__restrict__ lse, int Hkv, int G, int q_len, int Dv, int chunk_off_off)
+    float *__restrict__ lse, int Hkv, int G, int q_len, int Dv, int chunk_off_off, int fixed_splits)
 {
     const int bh = blockIdx.x;
     const int b = bh / Hkv, h = bh % Hkv;
-    const int c0 = plan[chunk_off_off + b];
-    const int n = plan[chunk_off_off + b + 1] - c0;
+    // a fixed-split plan cuts every request into the same count (no plan read needed)
+    const int c0 = fixed_splits > 0 ? b * fixed_splits : plan[chunk_off_off + b];
+    const int n = fixed_splits > 0 ? fixed_splits : plan[chunk_off_off + b + 1] - c0;
     if (n == 1) return;                           // the decode kernel wrote this row
     merge_rows<1>(ws_o, ws_lse, sinks, out, lse, b, c0, n, Hkv * G, q_len, Dv, h * G, G,
                blockIdx.y * kCombineThreads + threadIdx.x, gridDim.y * kCombineThreads);
@@ -27,12 +28,12 @@ __global__ __launch_bounds__(kCombineThreads) void pa_combine_kernel(
 
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           const float *sinks, uint16_t *out, float *lse, int B, int Hkv, int G,
-                          int q_len, int Dv, int chunk_off_off, hipStream_t stream)
+                          int q_len, int Dv, int chunk_off_off, int fixed_splits, hipStream_t stream)
 {
     const int per_bh = q_len * G * (Dv / 4);
     const dim3 grid(B * Hkv, (per_bh + kCombineThreads - 1) / kCombineThreads);
     hipLaunchKernelGGL(pa_combine_kernel, grid, dim3(kCombineThreads), 0, stream, plan, ws_o,
-                       ws_lse, sinks, out, lse, Hkv, G, q_len, Dv, chunk_off_off);
+                       ws_lse, sinks, out, lse, Hkv, G, q_len, Dv, chunk_off_off, fixed_splits);
     return hipGetLastError();
 }
 

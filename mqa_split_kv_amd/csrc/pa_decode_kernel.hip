@@ -203,8 +203,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int koff = col * (int)a.s_tok_b + g4 * 16;
     const int voff = (lane / C::CPR) * (int)a.s_tok_b + (lane % C::CPR) * 16;
 
-    const int ib = plan[a.part_begin_off + part];
-    const int ie = plan[a.part_begin_off + part + 1];
+    // a fixed-split plan has exactly one item per part (no plan read on the critical path)
+    const int ib = a.fixed_splits > 0 ? part : plan[a.part_begin_off + part];
+    const int ie = a.fixed_splits > 0 ? part + 1 : plan[a.part_begin_off + part + 1];
 
     for (int it = ib; it < ie; it++) {
         const int b = plan[a.items_off + 4 * it + 0];

@@ -90,6 +90,8 @@ struct DecodeArgs {
     int window;                 // sliding window (0: off)
     int topk;                   // sparse key slots per request (0: dense)
     int num_parts, part_begin_off, items_off, chunk_off_off;
+    int fixed_splits;           // s > 0: a fixed-split plan, part p is exactly item p (and
+                                // request b's chunks are b*s .. b*s+s-1); 0: balanced
     int32_t *counters;          // plan counter words; non-null: fused combine
     float scale_log2;           // logit scale * log2(e)
     int kv_format;
@@ -104,6 +106,6 @@ hipError_t launch_append(const pa_decode_desc *d, int n_new, const void *k_new, 
                          void *v_pool, float *k_scale, float *v_scale, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           const float *sinks, uint16_t *out, float *lse, int B, int Hkv, int G,
-                          int q_len, int Dv, int chunk_off_off, hipStream_t stream);
+                          int q_len, int Dv, int chunk_off_off, int fixed_splits, hipStream_t stream);
 
 }  // namespace pa

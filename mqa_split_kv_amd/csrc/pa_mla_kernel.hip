@@ -310,8 +310,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint32_t sc_off = (uint32_t)(8 * g4 * kRawRow + 512);
     const uint32_t pv_off = (uint32_t)((8 * g4 + ((lane & 15) >> 1)) * kRawRow + 8 * (lane & 1));
 
-    const int ib = plan[a.part_begin_off + part];
-    const int ie = plan[a.part_begin_off + part + 1];
+    // a fixed-split plan has exactly one item per part (no plan read on the critical path)
+    const int ib = a.fixed_splits > 0 ? part : plan[a.part_begin_off + part];
+    const int ie = a.fixed_splits > 0 ? part + 1 : plan[a.part_begin_off + part + 1];
 
     for (int it = ib; it < ie; it++) {
         const int b = plan[a.items_off + 4 * it + 0];
