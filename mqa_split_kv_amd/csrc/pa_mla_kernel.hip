@@ -29,9 +29,9 @@
 //   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
 //     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 5-slot
 //     ring of 752-byte rows (the stride at which both operand read patterns below run at
-//     the LDS's measured best); tile i+3's loads go out in iteration i, each wave putting
-//     its own between its MFMAs.  Page ids come the same way, 3 tiles ahead, into a small
-//     LDS ring (a scalar load would make every later LDS wait also wait for it);
+//     the LDS's measured best); tile i+3's loads go out at the top of iteration i.  Page ids
+//     come the same way, 3 tiles ahead, into a small LDS ring (a scalar load would make
+//     every later LDS wait also wait for it);
 //   * scores: the FP8 codes enter a scaled fp8 MFMA 16x16x128 as they are; Q is resident as
 //     two e4m3 terms with power-of-two scales per head and tile (q = hi 2^e_hi + lo 2^e_lo,
 //     exact to 2^-21 of the tile's max), so each 128-dim tile is two MFMAs.  The rope dims
@@ -368,34 +368,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             return pg;
         };
 
-        // ---- dense loads of tile t: the wave's 4 tokens are consecutive slots of one page;
-        //      dn_prep makes their first address, dn_part(k) loads token k (k < 4) or the page
-        //      id of tile t + kAhead (k = 4).  In the tile loop each wave puts its parts
-        //      between its MFMAs: issued at once after the barrier, the 8 waves' loads would
-        //      queue behind each other at the CU's memory port.
-        const uint8_t *d_tok = a.k_pool;
-        int d_nreal = 0, d_t = 0;
-        uint32_t d_lds0 = 0;
-        auto dn_prep = [&](int t, int page) {
-            const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 4 tokens
-            d_tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
-            d_nreal = min(max(t1 - tw, 0), kTokPerWave);
-            d_lds0 = lds_addr(&raw[t % kRawSlots][kTokPerWave * wave * kRawRow]);
-            d_t = t;
-        };
-        auto dn_part = [&](int k) {
-            if (k < kTokPerWave) {
-                if (lane < kChunks)
-                    lds_dma_buf16(d_tok + (int64_t)k * a.s_tok_b, k < d_nreal ? kTokBytes : 0, 16 * lane, d_lds0 + k * kRawRow);
-            } else {
-                dn_issue_page(d_t + kAhead);
-            }
-        };
-        auto dn_rest = [&]() {                     // all parts (a role with no MFMAs this tile)
-#pragma unroll
-            for (int k = 0; k <= kTokPerWave; k++) dn_part(k);
-        };
-
         // ---- loads of tile t into its ring slot: token tt of the wave (tile row 4 wave + tt)
         //      by lanes 0-40 through a buffer over that token's 656 bytes, or over none (reads
         //      as zeros) when it is not real.  Sparse: the page ids of tile t + kAhead and the
@@ -421,24 +393,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 if (lane == 0) s_valid[t % kRawSlots][wave] = (uint8_t)vm;
             } else {
-                dn_prep(t, page);
+                // the 4 tokens are consecutive slots of one page
+                const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 4 tokens
+                const uint8_t *tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
+                const int nreal = min(max(t1 - tw, 0), kTokPerWave);
+                const uint32_t lds0 = lds_addr(dst);
 #pragma unroll
-                for (int k = 0; k <= kTokPerWave; k++) dn_part(k);
+                for (int tt = 0; tt < kTokPerWave; tt++)
+                    if (lane < kChunks)
+                        lds_dma_buf16(tok + (int64_t)tt * a.s_tok_b, tt < nreal ? kTokBytes : 0, 16 * lane, lds0 + tt * kRawRow);
+                dn_issue_page(t + kAhead);
             }
         };
 
         // ---- top of tile i (both roles, same barriers): tile i's loads in (tiles i+1 ..
         //      i+kAhead-1 are younger), all waves past tile i-1 (slot of tile i-2 free, the
-        //      B operands of tile i-1 stored), then tile i+kAhead's loads into its slot
-        //      (dense: prepared here, issued by the role between its MFMAs; every wave issues
-        //      exactly one tile's loads per iteration, which the wait counts rely on)
+        //      B operands of tile i-1 stored), then tile i+kAhead's loads into its slot (every
+        //      wave issues exactly one tile's loads per iteration, which the wait counts rely
+        //      on; issued here or spread between the MFMAs measured the same)
         auto tile_top = [&](int i) {
             wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
             if (SPARSE) {
                 lds_barrier();
                 issue_tile(i + kAhead, 0);
             } else {
-                dn_prep(i + kAhead, page_barrier(i + kAhead));
+                issue_tile(i + kAhead, page_barrier(i + kAhead));
             }
         };
 
@@ -504,7 +483,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                 tile_top(i);
                 if (i == ntiles) {
-                    if (!SPARSE) dn_rest();
                     break;
                 }
                 PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[i % kRawSlots];
@@ -559,7 +537,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         }
                         // row block 0's combine runs under row block 1's MFMAs
                         if (sb == 1 && k >= 1 && k < 5) combine(0, k - 1);
-                        if (!SPARSE && sb == 0 && k <= kTokPerWave) dn_part(k);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -654,7 +631,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                 tile_top(i);
                 if (i == 0) {
-                    if (!SPARSE) dn_rest();
                     PA_LDS uint8_t *vb0 = vbase(0);
 #pragma unroll
                     for (int d = 0; d < kVPre; d++) vw[d] = rd(vb0, d);
@@ -685,7 +661,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         const i32x2 w = vw[(db + 2) % kVRing];
                         va[(db + 2) % 3] = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
                     }
-                    if (!SPARSE && (db & 3) == 0 && db / 4 <= kTokPerWave) dn_part(db / 4);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (i < ntiles) {
