@@ -98,6 +98,7 @@ constexpr int kAhead = kRawSlots - 2;              // loads go out 3 tiles ahead
                                                    // 3 (sparse: positions 6) tiles ahead
 constexpr int kLookRing = 8;                       // lookup slots (tiles) per wave
 constexpr int kDvBlocks = kDv / 16;                // 32 PV MFMAs per tile and value wave
+constexpr int kVBlocks = 128 / 16;                 // 16-dim blocks of a value wave's value tile
 constexpr float kLazyMax = 8.0f;                   // log2 units
 
 static_assert(kRawSlots >= 4, "the tile loop reads tiles i and i-1 with loads in flight");
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         //      wave issues exactly one tile's loads per iteration, which the wait counts rely
         //      on; issued here or spread between the MFMAs measured the same)
         auto tile_top = [&](int i) {
-            wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
+            wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
             if (SPARSE) {
                 lds_barrier();
                 issue_tile(i + kAhead, 0);
@@ -480,18 +481,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             float m = -INFINITY;     // reference max (log2 domain) of head `col`
             float l = 0.f;
 
-            for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
-                tile_top(i);
-                if (i == ntiles) {
-                    break;
-                }
-                PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[i % kRawSlots];
-                // ---- S^T of tile i (rows: this lane's tokens 8g4 + 4sb + r): one partial per
-                //      128-dim scale tile u (two scaled fp8 MFMAs 16x16x128, Q's hi and lo
-                //      terms) and one for the rope dims (two bf16 MFMAs 16x16x32), combined with
-                //      the token scales in fp32.  MFMA slot k of row block sb: tiles (0,1) hi,
-                //      (0,1) lo, (2,3) hi, (2,3) lo, rope 0, 1; every operand is read two slots
-                //      before its first use.
+            // ---- S^T of tile t (rows: this lane's tokens 8g4 + 4sb + r) into st[8]: one partial
+            //      per 128-dim scale tile u (two scaled fp8 MFMAs 16x16x128, Q's hi and lo
+            //      terms) and one for the rope dims (two bf16 MFMAs 16x16x32), combined with
+            //      the token scales in fp32 as each pair of tiles completes.  MFMA slot k of row
+            //      block sb: rope 0, 1, tiles (0,1) hi, (0,1) lo, (2,3) hi, (2,3) lo; every
+            //      operand is read two slots before its first use.  step(s) runs in slot
+            //      s = 10 sb + k, after its MFMA: the VALU work of the previous tile, issued
+            //      while the matrix core works.
+            auto qk_tile = [&](int t, float (&st)[8], auto &&step) {
+                PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t % kRawSlots];
                 auto rd_codes = [&](int sb, int u) {
                     PA_LDS const uint8_t *p = slot + qk_off + 4 * sb * kRawRow + 128 * u;
                     const u32x4 x = *(PA_LDS const u32x4 *)p;
@@ -499,19 +498,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
                 };
                 auto rd_rope = [&](int sb, int r) { return *(PA_LDS const bf16x8 *)(slot + rope_off + 4 * sb * kRawRow + 64 * r); };
-                float st[8];
-                f32x4 sc_tok[8];                   // token 8g4 + r's four tile scales
                 i32x8 kc[2][4];
                 bf16x8 kr[2][2];
                 f32x4 part[2][5];
-                kc[0][0] = rd_codes(0, 0);
-                kc[0][1] = rd_codes(0, 1);
-                // row r of row block sb: the token scales times the tile partials, plus rope
-                auto combine = [&](int sb, int r) {
-                    float x = part[sb][4][r];
+                f32x4 sc[8];                       // token 8g4 + r's four tile scales
+                kr[0][0] = rd_rope(0, 0);
+                kr[0][1] = rd_rope(0, 1);
+                // rows 2h, 2h+1 of row block sb, tiles 2v and 2v+1: the token scales times the
+                // tile partials, added to the rope partial (v = 0) or the sum so far (v = 1)
+                auto combine = [&](int sb, int v, int h) {
 #pragma unroll
-                    for (int u = 0; u < 4; u++) x += sc_tok[4 * sb + r][u] * part[sb][u][r];
-                    st[4 * sb + r] = x;
+                    for (int r = 2 * h; r < 2 * h + 2; r++) {
+                        float x = v == 0 ? part[sb][4][r] : st[4 * sb + r];
+#pragma unroll
+                        for (int u = 2 * v; u < 2 * v + 2; u++) x += sc[4 * sb + r][u] * part[sb][u][r];
+                        st[4 * sb + r] = x;
+                    }
                 };
 #pragma unroll
                 for (int sb = 0; sb < 2; sb++) {
@@ -520,67 +522,118 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                     for (int k = 0; k < 10; k++) {
                         // reads issued at this slot (the token scales early, for the combine)
-                        if (k == 0) kc[sb][2] = rd_codes(sb, 2);
-                        if (k == 1) kc[sb][3] = rd_codes(sb, 3);
+                        if (k == 0) kc[sb][0] = rd_codes(sb, 0);
+                        if (k == 1) kc[sb][1] = rd_codes(sb, 1);
                         if (k >= 2 && k < 6)
-                            sc_tok[4 * sb + k - 2] = *(PA_LDS const f32x4 *)(slot + sc_off + (4 * sb + k - 2) * kRawRow);
-                        if (k == 6) kr[sb][0] = rd_rope(sb, 0);
-                        if (k == 7) kr[sb][1] = rd_rope(sb, 1);
-                        if (sb == 0 && k == 8) kc[1][0] = rd_codes(1, 0);
-                        if (sb == 0 && k == 9) kc[1][1] = rd_codes(1, 1);
-                        if (k < 8) {
-                            const int u = 2 * (k >> 2) + (k & 1);
-                            const bool lo = (k & 2) != 0;
-                            part[sb][u] = mfma_fp8_q(u, kc[sb][u], lo ? qlo[u] : qhi[u], part[sb][u], lo ? qsc_lo : qsc_hi);
+                            sc[4 * sb + k - 2] = *(PA_LDS const f32x4 *)(slot + sc_off + (4 * sb + k - 2) * kRawRow);
+                        if (k == 4) kc[sb][2] = rd_codes(sb, 2);
+                        if (k == 5) kc[sb][3] = rd_codes(sb, 3);
+                        if (sb == 0 && k == 8) kr[1][0] = rd_rope(1, 0);
+                        if (sb == 0 && k == 9) kr[1][1] = rd_rope(1, 1);
+                        if (k < 2) {
+                            part[sb][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k], qrope[k], part[sb][4], 0, 0, 0);
                         } else {
-                            part[sb][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k - 8], qrope[k - 8], part[sb][4], 0, 0, 0);
+                            const int u = 2 * ((k - 2) >> 2) + (k & 1);
+                            const bool lo = ((k - 2) & 2) != 0;
+                            part[sb][u] = mfma_fp8_q(u, kc[sb][u], lo ? qlo[u] : qhi[u], part[sb][u], lo ? qsc_lo : qsc_hi);
                         }
-                        // row block 0's combine runs under row block 1's MFMAs
-                        if (sb == 1 && k >= 1 && k < 5) combine(0, k - 1);
+                        // tiles 0, 1 two slots after their last MFMA; tiles 2, 3 of row block
+                        // 0 under row block 1's first MFMAs
+                        if (k == 7 || k == 8) combine(sb, 0, k - 7);
+                        if (sb == 1 && (k == 1 || k == 2)) combine(0, 1, k - 1);
+                        step(10 * sb + k);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-#pragma unroll
-                for (int r = 0; r < 4; r++) combine(1, r);
-                // ---- softmax: logits and mask, the max over the head's 32 tokens, the
-                //      lazily moved reference, p = 2^(s - m) and the row sum; P and the factor
-                //      for O^T (1 unless the reference moved) go to the value wave
+                combine(1, 1, 0);
+                combine(1, 1, 1);
+            };
+
+            float st_cur[8];                   // S^T of the tile whose softmax is next
+            for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
+                tile_top(i);                   // tiles i and i + 1 are in LDS
+                if (i == ntiles) {
+                    break;
+                }
+                if (i == 0) qk_tile(0, st_cur, [](int) {});
+                // ---- softmax of tile i, spread over the MFMA slots of tile i + 1's S^T: logits
+                //      and mask, the max over the head's 32 tokens, the lazily moved reference,
+                //      p = 2^(s - m) and the row sum; P and the factor for O^T (1 unless the
+                //      reference moved) go to the value wave.  (Past the last tile, tile i + 1's
+                //      slot holds zeros and its result is unused.)
                 uint32_t vmask = 0;
                 if (SPARSE) {                      // tokens 8g4 .. 8g4+7: waves 2g4, 2g4+1
                     const uint32_t v2 = *(const uint16_t *)&s_valid[i % kRawSlots][2 * g4];
                     vmask = (v2 & 0xFu) | ((v2 >> 4) & 0xF0u);
                 }
-                float sv[8], bm = -INFINITY;
+                float sv[8], bm = -INFINITY, m_new = m, alpha = 1.f, mref = 0.f, ps = 0.f;
+                float pr[8];
+                f32x4 scr[8];                      // tile i's token scales, read again
+                bf16x8 pb[4];
+                auto logits = [&](int r0) {
 #pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    const int tok = t0 + kT * i + 8 * g4 + r;
-                    const bool vis = SPARSE ? ((vmask >> r) & 1u) != 0
-                                            : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
-                    sv[r] = vis ? st[r] * a.scale_log2 : -INFINITY;
-                    bm = fmaxf(bm, sv[r]);
-                }
-                bm = col_max(bm);
-                const float m_new = bm > m + kLazyMax ? bm : m;
-                const float alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
-                const float mref = m_new == -INFINITY ? 0.f : m_new;
-                float pr[8], ps = 0.f;
+                    for (int r = r0; r < r0 + 4; r++) {
+                        const int tok = t0 + kT * i + 8 * g4 + r;
+                        const bool vis = SPARSE ? ((vmask >> r) & 1u) != 0
+                                                : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
+                        sv[r] = vis ? st_cur[r] * a.scale_log2 : -INFINITY;
+                        bm = fmaxf(bm, sv[r]);
+                    }
+                };
+                auto softmax_step = [&](int s) {
+                    if (s == 0) logits(0);
+                    if (s == 1) logits(4);
+                    if (s == 2) {
+                        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+                        bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+                    }
+                    if (s == 3) {
+                        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+                        bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+                        m_new = bm > m + kLazyMax ? bm : m;
+                        alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
+                        mref = m_new == -INFINITY ? 0.f : m_new;
+                    }
+                    if (s >= 4 && s < 8) {
 #pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    pr[r] = fast_exp2(sv[r] - mref);
-                    ps += pr[r];
-                }
-                l = l * alpha + ps;
-                m = m_new;
-                // the value wave's B operands: P^T times each value tile's token scales (the
-                // value is the key's first 512 dims, so the scales are the key tile scales)
+                        for (int r = 2 * (s - 4); r < 2 * (s - 4) + 2; r++) {
+                            pr[r] = fast_exp2(sv[r] - mref);
+                            ps += pr[r];
+                        }
+                    }
+                    if (s == 8) {
+                        l = l * alpha + ps;
+                        m = m_new;
+                    }
+                    // the value wave's B operands: P^T times each value tile's token scales
+                    // (the value is the key's first 512 dims, so the scales are the key tile
+                    // scales), two rows per slot, from scales read again four slots before
+                    if (s >= 5 && s < 9) {
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    bf16x8 pb;
+                        for (int r = 2 * (s - 5); r < 2 * (s - 5) + 2; r++)
+                            scr[r] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + r * kRawRow);
+                    }
+                    if (s >= 9 && s < 13) {
 #pragma unroll
-                    for (int r = 0; r < 8; r++) pb[r] = (__bf16)(pr[r] * sc_tok[r][t]);
-                    s_p[i & 1][hg][t][lane] = pb;
-                }
-                if (g4 == 0) s_alpha[i & 1][hg][col] = alpha;
+                        for (int r = 2 * (s - 9); r < 2 * (s - 9) + 2; r++) {
+#pragma unroll
+                            for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * scr[r][t]);
+                        }
+                    }
+                    if (s == 13) {
+                        s_p[i & 1][hg][0][lane] = pb[0];
+                        s_p[i & 1][hg][1][lane] = pb[1];
+                    }
+                    if (s == 14) {
+                        s_p[i & 1][hg][2][lane] = pb[2];
+                        s_p[i & 1][hg][3][lane] = pb[3];
+                        if (g4 == 0) s_alpha[i & 1][hg][col] = alpha;
+                    }
+                };
+                float st_nxt[8];
+                qk_tile(i + 1, st_nxt, softmax_step);
+#pragma unroll
+                for (int r = 0; r < 8; r++) st_cur[r] = st_nxt[r];
             }
 
             // ---- epilogue: 1 / l (with a sink of a whole-request item) and lse
@@ -608,85 +661,89 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             lds_barrier();                                   // s_inv out
         } else {
-            // ================= value wave: O^T += V^T P^T of tile i-1 in iteration i
+            // ================= value wave: O^T += V^T P^T of tile i-1 in iteration i, for
+            // value tile vt = hg (dims 128 vt .. +127) and all 4 head blocks: O^T block
+            // acc[4 d + hb] holds dims 128 vt + 16 d + (4 g4 + e) of head col of block hb, so
+            // each V^T operand is read and converted once and feeds 4 MFMAs
+            const int vt = hg;
             f32x4 acc[kDvBlocks];
 #pragma unroll
             for (int d = 0; d < kDvBlocks; d++) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            // V^T reads: tile j's value dims 16db + col, tokens 8g4 + 0..7 (lane), kept kVPre
-            // MFMAs ahead in a ring; the first kVPre of the next tile go out before the barrier
-            // (the tile is in LDS since the top of this iteration)
-            constexpr int kVPre = 6, kVRing = 8;
+            // V^T reads: tile j's dims 128 vt + 16 d + col, tokens 8g4 + 0..7 (lane); the 8
+            // reads of the next tile go out before the barrier (the tile is in LDS since the
+            // top of this iteration)
             // (the base is made opaque, so that the reads become base + immediate offset and
             // the compiler does not hoist a register per read)
             auto vbase = [&](int t) {
-                uint32_t x = lds_addr(raw[t % kRawSlots]) + pv_off;
+                uint32_t x = lds_addr(raw[t % kRawSlots]) + pv_off + 128 * vt;
                 asm volatile("" : "+v"(x));
                 return (PA_LDS uint8_t *)(uintptr_t)x;
             };
-            auto rd = [&](PA_LDS uint8_t *vb, int db) {
-                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2 *)(vb + 16 * db));
+            auto rd = [&](PA_LDS uint8_t *vb, int d) {
+                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2 *)(vb + 16 * d));
             };
-            i32x2 vw[kVRing];
+            i32x2 vw[kVBlocks];
             for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                 tile_top(i);
-                if (i == 0) {
-                    PA_LDS uint8_t *vb0 = vbase(0);
+                if (i > 0) {
+                    const int j = i - 1;
+                    // the tile's factors for O^T and the B operands (P^T of head block hb
+                    // times value tile vt's token scales, from the score wave of hb)
+                    float alpha[4];
+                    bf16x8 pbt[4];
 #pragma unroll
-                    for (int d = 0; d < kVPre; d++) vw[d] = rd(vb0, d);
-                    continue;
-                }
-                const int j = i - 1;
-                PA_LDS uint8_t *vb = vbase(j);
-                // the tile's factor for O^T and the B operands (P^T times value tile t's token
-                // scales, from the score wave), read together
-                const float alpha = s_alpha[j & 1][hg][col];
-                bf16x8 pbt[4];
-#pragma unroll
-                for (int t = 0; t < 4; t++) pbt[t] = s_p[j & 1][hg][t][lane];
-                if (__any(alpha != 1.f)) {                   // rare: the reference moved
-                    mfma_acc_drain(acc);
-#pragma unroll
-                    for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha;
-                }
-                // A = V^T converted to bf16 two MFMAs ahead (no wait states before the MFMA)
-                bf16x8 va[3];
-                va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
-                va[1] = fp8x8_to_bf16((uint32_t)vw[1][0], (uint32_t)vw[1][1]);
-#pragma unroll
-                for (int db = 0; db < kDvBlocks; db++) {
-                    if (db + kVPre < kDvBlocks) vw[(db + kVPre) % kVRing] = rd(vb, db + kVPre);
-                    mfma_acc(acc[db], va[db % 3], pbt[db >> 3]);
-                    if (db + 2 < kDvBlocks) {
-                        const i32x2 w = vw[(db + 2) % kVRing];
-                        va[(db + 2) % 3] = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+                    for (int hb = 0; hb < 4; hb++) {
+                        alpha[hb] = s_alpha[j & 1][hb][col];
+                        pbt[hb] = s_p[j & 1][hb][vt][lane];
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                    if (__any(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
+                        mfma_acc_drain(acc);                 // rare: a reference moved
+#pragma unroll
+                        for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha[d & 3];
+                    }
+                    // A = V^T converted to bf16 two blocks ahead (no wait states before the MFMA)
+                    bf16x8 va[3];
+                    va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
+                    va[1] = fp8x8_to_bf16((uint32_t)vw[1][0], (uint32_t)vw[1][1]);
+#pragma unroll
+                    for (int d = 0; d < kVBlocks; d++) {
+#pragma unroll
+                        for (int hb = 0; hb < 4; hb++) mfma_acc(acc[4 * d + hb], va[d % 3], pbt[hb]);
+                        if (d + 2 < kVBlocks)
+                            va[(d + 2) % 3] = fp8x8_to_bf16((uint32_t)vw[d + 2][0], (uint32_t)vw[d + 2][1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
                 if (i < ntiles) {
                     PA_LDS uint8_t *vbn = vbase(i);
 #pragma unroll
-                    for (int d = 0; d < kVPre; d++) vw[d] = rd(vbn, d);
+                    for (int d = 0; d < kVBlocks; d++) vw[d] = rd(vbn, d);
                 }
             }
             mfma_acc_drain(acc);
             lds_barrier();                                   // s_inv in
-            const float inv = s_inv[hg][col];
-            // ---- epilogue: O^T layout: lane holds dims 16db + 4g4 + e of head `col`
-            if (active) {
-                if (flags & 1) {
-                    uint16_t *orow = a.out + ((int64_t)b * nq * Hq + qr) * kDv + 4 * g4;
+            // ---- epilogue: rows of head block hb: draft token and heads as in the score wave
 #pragma unroll
-                    for (int db = 0; db < kDvBlocks; db++) {
+            for (int hb = 0; hb < 4; hb++) {
+                const int r0 = group * kHeadsPerWG + hb * kHeadsPerWave;
+                if (r0 >= G * nq) continue;                  // no query rows
+                const int q_i = r0 / G;
+                const int64_t row = (int64_t)q_i * Hq + (r0 - q_i * G) + col;
+                const float inv = s_inv[hb][col];
+                if (flags & 1) {
+                    uint16_t *orow = a.out + ((int64_t)b * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
+#pragma unroll
+                    for (int d = 0; d < kVBlocks; d++) {
                         bf16x4 o;
 #pragma unroll
-                        for (int e = 0; e < 4; e++) o[e] = (__bf16)(acc[db][e] * inv);
-                        *(bf16x4 *)(orow + 16 * db) = o;
+                        for (int e = 0; e < 4; e++) o[e] = (__bf16)(acc[4 * d + hb][e] * inv);
+                        *(bf16x4 *)(orow + 16 * d) = o;
                     }
                 } else {
-                    float *orow = a.ws_o + ((int64_t)it * nq * Hq + qr) * kDv + 4 * g4;
+                    float *orow = a.ws_o + ((int64_t)it * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
 #pragma unroll
-                    for (int db = 0; db < kDvBlocks; db++) *(f32x4 *)(orow + 16 * db) = acc[db] * inv;
+                    for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
                 }
             }
         }
