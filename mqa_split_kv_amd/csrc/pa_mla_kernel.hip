@@ -512,6 +512,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         float x = v == 0 ? part[sb][4][r] : st[4 * sb + r];
 #pragma unroll
                         for (int u = 2 * v; u < 2 * v + 2; u++) x += sc[4 * sb + r][u] * part[sb][u][r];
+                        asm volatile("" : "+v"(x));    // computed in this slot
                         st[4 * sb + r] = x;
                     }
                 };
@@ -627,7 +628,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     if (s == 14) {
                         s_p[i & 1][hg][2][lane] = pb[2];
                         s_p[i & 1][hg][3][lane] = pb[3];
-                        if (g4 == 0) s_alpha[i & 1][hg][col] = alpha;
+                        // (the column's 4 lanes hold the same factor: no branch in the body, which
+                        // would let the compiler sink the MFMAs and their combines past it)
+                        s_alpha[i & 1][hg][col] = alpha;
                     }
                 };
                 float st_nxt[8];
