@@ -487,8 +487,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             //      the token scales in fp32 as each pair of tiles completes.  MFMA slot k of row
             //      block sb: rope 0, 1, tiles (0,1) hi, (0,1) lo, (2,3) hi, (2,3) lo; every
             //      operand is read two slots before its first use.  step(s) runs in slot
-            //      s = 10 sb + k, after its MFMA: the VALU work of the previous tile, issued
-            //      while the matrix core works.
+            //      s = 10 sb + k, before its MFMA: the VALU work of the previous tile, issued
+            //      while the matrix core works (and, first, while the tile's first reads
+            //      are on their way).
             auto qk_tile = [&](int t, float (&st)[8], auto &&step) {
                 PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t % kRawSlots];
                 auto rd_codes = [&](int sb, int u) {
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         if (k == 5) kc[sb][3] = rd_codes(sb, 3);
                         if (sb == 0 && k == 8) kr[1][0] = rd_rope(1, 0);
                         if (sb == 0 && k == 9) kr[1][1] = rd_rope(1, 1);
+                        step(10 * sb + k);
                         if (k < 2) {
                             part[sb][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k], qrope[k], part[sb][4], 0, 0, 0);
                         } else {
@@ -542,7 +544,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         // 0 under row block 1's first MFMAs
                         if (k == 7 || k == 8) combine(sb, 0, k - 7);
                         if (sb == 1 && (k == 1 || k == 2)) combine(0, 1, k - 1);
-                        step(10 * sb + k);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
