@@ -14,22 +14,25 @@
 // between two 64-head CTAs through a cluster, section 计算环节一; here the L2 of the XCD
 // plays that role).
 //
-// Waves hg and hg + 4 share a SIMD and one block of 16 query heads, with two roles (the
-// FlashMLA walk-through splits a tile's work over two warpgroups, section 计算环节二; here
-// the split is by operation):
-//   * the score wave (Q resident) computes S^T[32 tok x 16 heads] = K . Q^T of tile i and
-//     its softmax in iteration i, and hands the PV operands to the value wave through LDS;
-//   * the value wave (O^T[512 x 16 heads] resident) runs O^T += V^T . P^T of tile i-1 in
-//     iteration i.
+// Waves hg and hg + 4 share a SIMD, with two roles (the FlashMLA walk-through splits a
+// tile's work over two warpgroups, section 计算环节二; here the split is by operation):
+//   * score wave hg (Q of head block hg resident) computes S^T[32 tok x 16 heads] = K . Q^T;
+//     in iteration i it runs tile i+1's MFMAs and, between them, tile i's softmax, and hands
+//     P^T of tile i to the value waves through LDS;
+//   * value wave hg (O^T of value dims 128 hg .. +127 for all 64 heads resident, 128
+//     registers) runs O^T += V^T . P^T of tile i-1 in iteration i: each V^T operand is read
+//     and converted once and feeds the 4 head blocks' MFMAs.
 // Two waves per SIMD let one wave's conversions, softmax and waits run under the other's
-// matrix work, which one wave cannot do for itself (a wave's dependent VALU chains and its
-// LDS and barrier waits stall its own MFMA issue).
+// matrix work; the score wave also overlaps its own softmax with its next tile's MFMAs (a
+// wave's dependent VALU chains and its LDS and barrier waits otherwise stall its own MFMA
+// issue).
 //
 // Per 32-token tile:
 //   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
 //     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 5-slot
 //     ring of 752-byte rows (the stride at which both operand read patterns below run at
-//     the LDS's measured best); tile i+3's loads go out at the top of iteration i.  Page ids
+//     the LDS's measured best); tile i+3's loads go out at the top of iteration i, after
+//     the wait for tiles i and i+1 (the score waves read tile i+1's keys).  Page ids
 //     come the same way, 3 tiles ahead, into a small LDS ring (a scalar load would make
 //     every later LDS wait also wait for it);
 //   * scores: the FP8 codes enter a scaled fp8 MFMA 16x16x128 as they are; Q is resident as
@@ -39,9 +42,10 @@
 //     partials: S = sum_t scale_t (q_t . k_t) + q_rope . k_rope.  (The FlashMLA walk-through
 //     dequantises to bf16 and runs bf16 MMA with fp32 accumulation, section 计算环节一; here
 //     no operand of the score product is converted.)
-//   * an online softmax per head column; the score wave writes P^T times each 128-dim value
-//     tile's token scales (bf16, the B operands of the PV MFMAs) and the factor for O^T (1
-//     unless the reference max moved);
+//   * an online softmax per head column (the previous tile's, in the MFMA slots of the next
+//     tile's scores); the score wave writes P^T times each 128-dim value tile's token scales
+//     (bf16, the B operands of the PV MFMAs) and the factor for O^T (1 unless the reference
+//     max moved);
 //   * O^T += V^T . P^T with bf16 MFMA 16x16x32, V^T read transposed from the FP8 codes
 //     (ds_read_b64_tr_b8) and converted in registers (exact).  O^T takes 128 registers (the
 //     register-budget problem the FlashMLA walk-through describes in section 计算环节二),
@@ -49,7 +53,7 @@
 //     and the score wave's registers are VGPRs.
 // Operand layouts.  QK row block sb (0, 1) of the A operand holds, in MFMA row m = 4g + r,
 // token 8g + 4sb + r, so lane group g of the S^T result holds tokens 8g..8g+7: exactly the
-// k slots the same lanes of the value wave feed to the PV MFMA (B = P^T, k = 8g + j), and
+// k slots the same lanes of a value wave feed to the PV MFMA (B = P^T, k = 8g + j), and
 // the transposed read returns tokens 8g..8g+7 of one value dim per lane; the PV operands
 // pass through LDS lane for lane.  In the fp8 MFMA lane (col, g) holds dims 16g + 0..15
 // and 64 + 16g + 0..15 of the 128-dim tile.
