@@ -98,10 +98,11 @@ constexpr int kTokPerWave = kT / kWaves;           // 4 tokens loaded per wave a
 constexpr int kRawRow = 752;                       // LDS row of a token (656 + 96)
 constexpr int kRawTile = kT * kRawRow;             // 24064
 constexpr int kRawSlots = 5;                       // tile ring
-constexpr int kAhead = kRawSlots - 2;              // loads go out 3 tiles ahead; lookups: page ids
-                                                   // 3 (sparse: positions 6) tiles ahead
+constexpr int kAhead = kRawSlots - 2;              // loads go out 3 tiles ahead (2 ahead of the keys'
+                                                   // first use); lookups: page ids 3 (sparse:
+                                                   // positions 6) tiles ahead
 constexpr int kLookRing = 8;                       // lookup slots (tiles) per wave
-constexpr int kDvBlocks = kDv / 16;                // 32 PV MFMAs per tile and value wave
+constexpr int kDvBlocks = kDv / 16;                // O^T blocks of a value wave (8 dims x 4 heads), 32 MFMAs a tile
 constexpr int kVBlocks = 128 / 16;                 // 16-dim blocks of a value wave's value tile
 constexpr float kLazyMax = 8.0f;                   // log2 units
 
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int hg = wave & 3;                       // head block; waves hg and hg + 4 share a SIMD
+    const int hg = wave & 3;                       // score: head block; value: value tile (same SIMD)
     const bool scorer = wave < 4;                  // score wave; else value wave
     // workgroup id -> (part, head group): the head groups of one part are 8 ids apart
     const int wg = blockIdx.x;
@@ -611,7 +612,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         l = l * alpha + ps;
                         m = m_new;
                     }
-                    // the value wave's B operands: P^T times each value tile's token scales
+                    // the value waves' B operands: P^T times each value tile's token scales
                     // (the value is the key's first 512 dims, so the scales are the key tile
                     // scales), two rows per slot, from scales read again four slots before
                     if (s >= 5 && s < 9) {
