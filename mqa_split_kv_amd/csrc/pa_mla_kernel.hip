@@ -710,11 +710,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         mfma_acc_drain(acc);                 // rare: a reference moved
 #pragma unroll
                         for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha[d & 3];
+                        mfma_acc_drain(acc);                 // (wait states before the MFMAs)
                     }
-                    // A = V^T converted to bf16 two blocks ahead (no wait states before the MFMA)
+                    // A = V^T converted to bf16 two blocks ahead; the first two get their wait
+                    // states before the first MFMA explicitly (the asm MFMAs are invisible to
+                    // the compiler's hazard checks)
                     bf16x8 va[3];
                     va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
                     va[1] = fp8x8_to_bf16((uint32_t)vw[1][0], (uint32_t)vw[1][1]);
+                    asm volatile("s_nop 1" : "+v"(va[0]), "+v"(va[1]));
 #pragma unroll
                     for (int d = 0; d < kVBlocks; d++) {
 #pragma unroll
