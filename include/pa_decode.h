@@ -28,15 +28,16 @@
  *                      in one chunk, partials (workspace) for the others
  *   pa_decode_combine  LSE-weighted merge of the partials into out / lse
  *
- * With PA_FLAG_FUSED_COMBINE (bf16 and fp8 page-head formats) the merge runs inside
- * pa_decode_run instead: the workgroup that finishes the last chunk of a request
- * merges that request's chunks (the XQA article's "last CTA merges" variant, section
- * "归约怎么记"), found with a device-scope counter per (request, row group) kept in
- * the plan buffer; then pa_decode_combine has nothing to do and returns without
- * launching.  On MI355X this is slower than the separate combine kernel: the
- * device-scope release that publishes the partials writes back the L2 of the
- * workgroup's XCD (the 8 XCD caches are not coherent with each other), which costs
- * more than the combine launch it saves.
+ * With PA_FLAG_FUSED_COMBINE (bf16 and fp8 page-head formats; MLA-656 with q_len 1 and
+ * no sparse indices) the merge runs inside pa_decode_run instead: the workgroup that
+ * finishes the last chunk of a request merges that request's chunks (the XQA article's
+ * "last CTA merges" variant, section "归约怎么记"), found with a device-scope counter per
+ * (request, row group) kept in the plan buffer; then pa_decode_combine has nothing to do
+ * and returns without launching.  The partials are written and read with
+ * device-coherent (agent-scope) accesses, since the 8 XCD caches are not coherent with
+ * each other; on MI355X the merging workgroup then waits for those stores, the counter
+ * and the coherent reads in turn, which on small workloads costs more than the combine
+ * launch it saves.
  *
  * Ownership: the caller allocates and owns every buffer (device memory for all
  * array arguments).  The library never allocates, frees or synchronises; it keeps
@@ -81,7 +82,7 @@ typedef enum {
 
 enum {
     /* pa_decode_run merges the chunks itself; pa_decode_combine becomes a no-op.
-       Not for PA_KV_MLA656 (PA_ERR_UNSUPPORTED). */
+       PA_KV_MLA656: with q_len 1 and topk 0 only (else PA_ERR_UNSUPPORTED). */
     PA_FLAG_FUSED_COMBINE = 1
 };
 

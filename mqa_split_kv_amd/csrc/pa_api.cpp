@@ -69,9 +69,11 @@ pa_status check_desc(const pa_decode_desc *d)
     if (d->num_splits > 256) return PA_ERR_UNSUPPORTED;
     if ((int64_t)d->max_pages_per_seq * P > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
     if (d->kv_format == PA_KV_MLA656) {
-        // the MLA kernel keeps its whole register file for the tile loop; its chunks are
-        // merged by the combine kernel only
-        if (d->flags & PA_FLAG_FUSED_COMBINE) return PA_ERR_UNSUPPORTED;
+        // fused combine: one query token (a head group of the MLA kernel is then a range
+        // of heads, the unit the in-kernel merge works on), no sparse indices (the sparse
+        // variant has no registers to spare for it)
+        if ((d->flags & PA_FLAG_FUSED_COMBINE) && (d->q_len != 1 || d->topk > 0))
+            return PA_ERR_UNSUPPORTED;
         if (d->Hkv != 1 || d->D != 576 || d->Dv != 512) return PA_ERR_UNSUPPORTED;
         if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
         if (d->G * d->q_len > 1024) return PA_ERR_UNSUPPORTED;         // 16 groups of 64 rows

@@ -71,6 +71,7 @@
 // the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
 // applied in the softmax.
 #include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
@@ -284,6 +285,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ bf16x8 s_p[2][4][4][64];
     __shared__ float s_alpha[2][4][16];       // factor on O^T before the tile's PV, per head
     __shared__ float s_inv[4][16];            // the item's final 1 / l, per head
+    __shared__ int s_flag;                    // fused combine: this workgroup merges
     __shared__ __attribute__((aligned(4))) uint8_t s_valid[kRawSlots][kWaves];   // sparse: real-token bits
     // lookups: [position | page id][tile % kLookRing][wave][token] (dense: page ids of the
     // wave's first token only)
@@ -665,6 +667,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 s_inv[hg][col] = inv;
                 if (active) {
                     if (flags & 1) a.lse[(int64_t)b * nq * Hq + qr] = lse_v;
+                    else if (!SPARSE && a.counters) store_shared(a.ws_lse + (int64_t)it * nq * Hq + qr, lse_v);
                     else a.ws_lse[(int64_t)it * nq * Hq + qr] = lse_v;
                 }
             }
@@ -755,14 +758,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     }
                 } else {
                     float *orow = a.ws_o + ((int64_t)it * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
+                    if (!SPARSE && a.counters) {         // merged inside this launch
 #pragma unroll
-                    for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
+                        for (int d = 0; d < kVBlocks; d++) {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) store_shared(orow + 16 * d + e, acc[4 * d + hb][e] * inv);
+                        }
+                    } else {
+#pragma unroll
+                        for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
+                    }
                 }
             }
         }
         wait_vmcnt<0>();
         lds_barrier();                                       // the item's LDS is free
     }
+    // fused combine (dense, one query token: the head group is heads [64 group, 64 group +
+    // 64)): the last workgroup to finish a request's chunks merges them
+    if (!SPARSE && a.counters)
+        fused_combine_tail(a, plan, part, ib, ie, group, ngroups, group * kHeadsPerWG,
+                           min(kHeadsPerWG, G - group * kHeadsPerWG), 1, &s_flag);
 }
 
 }  // namespace

@@ -74,7 +74,9 @@ BAD = [
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
      pb.PA_ERR_UNSUPPORTED),
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
-          flags=1), pb.PA_ERR_UNSUPPORTED),      # MLA chunks merge in the combine kernel
+          flags=1, q_len=2), pb.PA_ERR_UNSUPPORTED),   # MLA fused merge: one query token
+    (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16,
+          flags=1, topk=64), pb.PA_ERR_UNSUPPORTED),   # ... and no sparse indices
 ]
 
 

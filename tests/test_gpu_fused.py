@@ -2,8 +2,8 @@
 
 With the flag, pa_decode_run merges the chunks itself (the last workgroup to finish a
 request's chunks merges them, XQA article, section "归约怎么记"), and
-pa_decode_combine does nothing (bf16 and fp8 page-head formats; the MLA format
-rejects the flag).  The merge arithmetic is the combine kernel's, so the
+pa_decode_combine does nothing (bf16 and fp8 page-head formats; the MLA format with one
+query token and no sparse indices).  The merge arithmetic is the combine kernel's, so the
 fused result must be bit-identical to run + separate combine, and within the parity bar
 of the oracle.  The counters the fused path uses live in the plan and must be back at
 zero after every run, so that one plan serves any number of runs.
@@ -90,12 +90,30 @@ def test_fused_changing_inputs_one_workspace(kw):
         _check_counters_zero(run)
 
 
-def test_fused_mla_is_unsupported():
-    """The MLA kernel's chunks are merged by the combine kernel only."""
-    case = _mla_case(lens=(300, 1, 64))
-    with pytest.raises(pb.PaDecodeError) as e:
-        GpuRun(case, fused=True)()
-    assert e.value.status == pb.PA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("kw", [dict(lens=(300, 1, 64)),
+                                dict(lens=(1000, 33), splits=3),
+                                dict(lens=(129, 2000), G=64, P=16),
+                                dict(lens=(0, 700, 0), G=32, P=128),
+                                dict(lens=(0, 700, 0), G=32, P=128, splits=4),
+                                dict(lens=(5000, 3), G=16, splits=256)])
+def test_fused_mla_equals_separate_and_oracle(kw):
+    case = _mla_case(**kw)
+    o_sep, l_sep = GpuRun(case)()
+    run = GpuRun(case, fused=True)
+    o_fu, l_fu = run()
+    assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
+    ref_out, ref_lse = oracle.decode(case)
+    assert_parity(case, o_fu, l_fu, ref_out, ref_lse)
+    _check_counters_zero(run)
+
+
+def test_fused_mla_config_sampled():
+    case = synth.config_case(4)
+    o_sep, l_sep = GpuRun(case)()
+    run = GpuRun(case, fused=True)
+    o_fu, l_fu = run()
+    assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
+    _check_counters_zero(run)
 
 
 def test_fused_ragged_fp8_config_sampled():
@@ -126,7 +144,7 @@ def test_fused_hd64_config(B):
 # ---------------------------------------------------------------------------- graph replay
 
 @pytest.mark.parametrize("fused,which", [(False, "hd64"), (True, "hd64"), (False, "ragged"),
-                                         (True, "ragged"), (False, "mla")])
+                                         (True, "ragged"), (False, "mla"), (True, "mla")])
 def test_graph_replay_matches_eager(fused, which):
     """Capture one step (run + combine) in a graph; every replay, with eager work and
     synchronisation in between, must reproduce the eager result bit for bit."""

@@ -131,6 +131,32 @@ def test_sinks_mla(splits):
     _check(case)
 
 
+@pytest.mark.parametrize("splits", [0, 3])
+def test_sinks_mla_fused_equals_separate(splits):
+    case = _mla_case((1000, 33, 0, 300), G=64, P=64, splits=splits)
+    case["sinks"] = _sinks(case)
+    o1, l1 = GpuRun(case)()
+    o2, l2 = _check(case, fused=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_window_mla_fused_equals_separate():
+    case = _mla_case((1000, 33, 300), G=32, P=64)
+    case["window"] = 200
+    o1, l1 = GpuRun(case)()
+    o2, l2 = _check(case, fused=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_sparse_mla_fused_is_unsupported():
+    case = _mla_case((1000, 33, 300), G=16)
+    case["topk"] = 64
+    case["indices"] = _indices(case, 64)
+    with pytest.raises(pb.PaDecodeError) as e:
+        GpuRun(case, fused=True)()
+    assert e.value.status == pb.PA_ERR_UNSUPPORTED
+
+
 # ------------------------------------------------------------------------------ sparse
 
 SPARSE = [
