@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     PA_OK = 0,
     PA_ERR_INVALID = 1,      /* null pointer, non-positive size, misaligned pointer/stride */
-    PA_ERR_UNSUPPORTED = 2,  /* a valid shape this build has no kernel for */
+    PA_ERR_UNSUPPORTED = 2,  /* a valid shape the library has no kernel for */
     PA_ERR_SIZE = 3,         /* plan or workspace smaller than the size query returned */
     PA_ERR_DEVICE = 4        /* a HIP call (device query, kernel launch) failed */
 } pa_status;

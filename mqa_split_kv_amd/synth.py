@@ -70,7 +70,7 @@ class CaseSpec:
 
 
 # The five workloads of the decode-attention scope table, by index.
-CONFIGS = {
+WORKLOADS = {
     0: CaseSpec(B=2, Hq=8, Hkv=1, D=64, Dv=64, page_size=16, seq_lens=(100, 257),
                 pool_pages=40, num_splits=1, name="tiny GQA paged decode"),
     1: CaseSpec(B=32, Hq=64, Hkv=8, D=128, Dv=128, page_size=64, seq_lens=(4096,) * 32,
@@ -203,7 +203,7 @@ def config_case(index: int, B: Optional[int] = None, seed: Optional[int] = None,
     batch of the two-batch HD64 workload (its pool is 6 pages per request)."""
     import dataclasses
 
-    spec = CONFIGS[index]
+    spec = WORKLOADS[index]
     if index == 2:
         B = 8 if B is None else B
         spec = dataclasses.replace(spec, B=B, seq_lens=(1536,) * B, pool_pages=6 * B)

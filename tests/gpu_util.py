@@ -34,7 +34,7 @@ def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
     return x.view(np.float32).astype(np.float64)
 
 
-class GpuRun:
+class DecodeRun:
     """Plan + decode + combine for one instance and split setting."""
 
     def __init__(self, case: dict, num_splits=None, dev=None, poison=True, fused=False):

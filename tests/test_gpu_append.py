@@ -9,7 +9,7 @@ import oracle
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity, to_device
+from gpu_util import DecodeRun, assert_parity, to_device
 from test_oracle_append import _case, _new_tokens
 
 pytestmark = pytest.mark.gpu
@@ -105,6 +105,6 @@ def test_append_then_speculative_decode(fmt):
     rng = np.random.default_rng(8)
     q = synth.f32_to_bf16_bits(rng.standard_normal((len(lens), n_new, 16, 128)).astype(np.float32))
     spec_case = dict(ref, q=q, q_len=n_new)
-    out, lse = GpuRun(spec_case)()
+    out, lse = DecodeRun(spec_case)()
     ref_out, ref_lse = oracle.decode(spec_case)
     assert_parity(spec_case, out, lse, ref_out, ref_lse)

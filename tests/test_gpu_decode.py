@@ -19,7 +19,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity, to_device
+from gpu_util import DecodeRun, assert_parity, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,7 @@ SMALL = [
 @pytest.mark.parametrize("kw", SMALL)
 def test_small_parity(kw):
     case = _case(**kw)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -104,7 +104,7 @@ def test_small_parity(kw):
 @pytest.mark.parametrize("splits", [1, 2])
 def test_tiny_config(splits):
     case = synth.config_case(0)
-    out, lse = GpuRun(case, num_splits=splits)()
+    out, lse = DecodeRun(case, num_splits=splits)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -112,21 +112,21 @@ def test_tiny_config(splits):
 @pytest.mark.parametrize("B", [1, 8])
 def test_hd64_config(B):
     case = synth.config_case(2, B=B)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_llama70b_config_full():
     case = synth.config_case(1)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_ragged_fp8_config_sampled():
     case = synth.config_case(3)
-    run = GpuRun(case)
+    run = DecodeRun(case)
     out, lse = run()
     B, Hkv, G = case["B"], case["Hkv"], case["G"]
     rng = np.random.default_rng(0)
@@ -152,7 +152,7 @@ def test_ragged_fp8_config_sampled():
 def test_combine_of_oracle_partials(splits):
     """Feed oracle partials (O_i = Ot_i / l_i, lse_i = m_i + ln l_i) to the combine kernel."""
     case = _case(Hq=16, Hkv=2, D=128, P=16, lens=(1000, 0, 70, 2500), splits=splits)
-    run = GpuRun(case)
+    run = DecodeRun(case)
     run.plan()
     words = run.plan_words()
     items = oplan.items_of(words)
@@ -209,7 +209,7 @@ def test_needle_tokens_at_boundaries(splits, fmt):
                 sc = case["k_scale"][page, h]
                 case["k_pool"][page, h, t % P] = synth.f32_to_e4m3_codes(u * 12.0 / sc)
     scale = 4.0 / math.sqrt(128)
-    out, lse = GpuRun(case)(scale=scale)
+    out, lse = DecodeRun(case)(scale=scale)
     ref_out, ref_lse = oracle.decode(case, scale=scale)
     assert_parity(case, out, lse, ref_out, ref_lse)
     # the planted token dominates: out is (close to) its value row
@@ -224,7 +224,7 @@ def test_needle_tokens_at_boundaries(splits, fmt):
 
 def test_bitwise_deterministic():
     case = _case(Hq=32, Hkv=8, D=128, P=16, lens=(3000, 17, 900, 4096))
-    run = GpuRun(case)
+    run = DecodeRun(case)
     o1, l1 = run()
     o2, l2 = run()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
@@ -234,7 +234,7 @@ def test_plan_reuse_across_layers():
     """One plan serves several decode launches with different q / pools (layers)."""
     c1 = _case(Hq=16, Hkv=2, D=128, P=32, lens=(700, 1200), seed=5)
     c2 = _case(Hq=16, Hkv=2, D=128, P=32, lens=(700, 1200), seed=6)
-    run = GpuRun(c1)
+    run = DecodeRun(c1)
     run.plan()
     for c in (c1, c2):
         run.dev = to_device(c)
@@ -271,14 +271,14 @@ MLA_SMALL = [
 @pytest.mark.parametrize("kw", MLA_SMALL)
 def test_mla_small_parity(kw):
     case = _mla_case(**kw)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_mla_config_full_sampled():
     case = synth.config_case(4)
-    run = GpuRun(case)
+    run = DecodeRun(case)
     out, lse = run()
     B = case["B"]
     pairs = np.zeros((B, 1), bool)
@@ -306,7 +306,7 @@ def test_mla_q_dynamic_range():
     q[0, 3] = 0.0
     q[1, 5, 256:384] = 0.0
     case["q"] = synth.f32_to_bf16_bits(q.astype(np.float32)).reshape(case["q"].shape)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -330,7 +330,7 @@ def test_mla_needle(splits):
         tok[512:528] = sc.view(np.uint8)
         tok[528:] = synth.f32_to_bf16_bits(x[512:]).view(np.uint8)
     scale = 8.0 / math.sqrt(576)          # needle logit ~16 vs spread ~1.3: weight of the rest < 1e-3
-    out, lse = GpuRun(case)(scale=scale)
+    out, lse = DecodeRun(case)(scale=scale)
     ref_out, ref_lse = oracle.decode(case, scale=scale)
     assert_parity(case, out, lse, ref_out, ref_lse)
     for b, t in targets.items():

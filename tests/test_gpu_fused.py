@@ -17,7 +17,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity, bf16_bits_to_f64, to_device
+from gpu_util import DecodeRun, assert_parity, bf16_bits_to_f64, to_device
 from test_gpu_decode import _case, _mla_case
 
 pytestmark = pytest.mark.gpu
@@ -51,8 +51,8 @@ def _check_counters_zero(run):
 @pytest.mark.parametrize("kw", FUSED_CASES)
 def test_fused_equals_separate_and_oracle(kw):
     case = _case(**kw)
-    o_sep, l_sep = GpuRun(case)()
-    run = GpuRun(case, fused=True)
+    o_sep, l_sep = DecodeRun(case)()
+    run = DecodeRun(case, fused=True)
     o_fu, l_fu = run()
     assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
     ref_out, ref_lse = oracle.decode(case)
@@ -62,7 +62,7 @@ def test_fused_equals_separate_and_oracle(kw):
 
 def test_fused_repeated_runs_one_plan():
     case = _case(Hq=32, Hkv=8, D=128, P=16, lens=(3000, 17, 900, 4096, 0, 65))
-    run = GpuRun(case, fused=True)
+    run = DecodeRun(case, fused=True)
     o1, l1 = run()
     for _ in range(3):
         run.step()
@@ -78,7 +78,7 @@ def test_fused_changing_inputs_one_workspace(kw):
     """Runs on one plan and workspace with different q and KV each time: the merging
     workgroup must see this launch's partials, never an earlier launch's."""
     cases = [_case(seed=s, **kw) for s in (21, 22, 23)]
-    run = GpuRun(cases[0], fused=True)
+    run = DecodeRun(cases[0], fused=True)
     run.plan()
     for c in cases + cases[:1]:
         run.dev = to_device(c)
@@ -98,8 +98,8 @@ def test_fused_changing_inputs_one_workspace(kw):
                                 dict(lens=(5000, 3), G=16, splits=256)])
 def test_fused_mla_equals_separate_and_oracle(kw):
     case = _mla_case(**kw)
-    o_sep, l_sep = GpuRun(case)()
-    run = GpuRun(case, fused=True)
+    o_sep, l_sep = DecodeRun(case)()
+    run = DecodeRun(case, fused=True)
     o_fu, l_fu = run()
     assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
     ref_out, ref_lse = oracle.decode(case)
@@ -109,8 +109,8 @@ def test_fused_mla_equals_separate_and_oracle(kw):
 
 def test_fused_mla_config_sampled():
     case = synth.config_case(4)
-    o_sep, l_sep = GpuRun(case)()
-    run = GpuRun(case, fused=True)
+    o_sep, l_sep = DecodeRun(case)()
+    run = DecodeRun(case, fused=True)
     o_fu, l_fu = run()
     assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
     _check_counters_zero(run)
@@ -118,7 +118,7 @@ def test_fused_mla_config_sampled():
 
 def test_fused_ragged_fp8_config_sampled():
     case = synth.config_case(3)
-    run = GpuRun(case, fused=True)
+    run = DecodeRun(case, fused=True)
     out, lse = run()
     B, Hkv, G = case["B"], case["Hkv"], case["G"]
     rng = np.random.default_rng(7)
@@ -136,7 +136,7 @@ def test_fused_ragged_fp8_config_sampled():
 @pytest.mark.parametrize("B", [1, 8])
 def test_fused_hd64_config(B):
     case = synth.config_case(2, B=B)
-    out, lse = GpuRun(case, fused=True)()
+    out, lse = DecodeRun(case, fused=True)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -154,7 +154,7 @@ def test_graph_replay_matches_eager(fused, which):
         case = _mla_case(lens=(1000, 0, 33, 2100), splits=0)
     else:
         case = _case(Hq=32, Hkv=8, D=128, P=16, lens=(3000, 17, 900, 4096, 0, 65))
-    run = GpuRun(case, fused=fused)
+    run = DecodeRun(case, fused=fused)
     o_ref, l_ref = run()                     # eager: plan + step
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -14,7 +14,7 @@ import torch
 
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, bf16_bits_to_f64
+from gpu_util import DecodeRun, bf16_bits_to_f64
 from test_gpu_decode import _case, _mla_case
 from test_oracle_variants import _indices
 
@@ -48,8 +48,8 @@ PERM_CASES = [
 @pytest.mark.parametrize("name,kw", PERM_CASES, ids=[c[0] for c in PERM_CASES])
 def test_page_permutation_bit_identical(name, kw):
     case = _case(pool_extra=9, **kw)
-    o1, l1 = GpuRun(case)()
-    o2, l2 = GpuRun(_permute_pages(case))()
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(_permute_pages(case))()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
@@ -58,15 +58,15 @@ def test_mla_page_permutation_bit_identical(sparse):
     case = _mla_case((1000, 33, 300), G=64, P=64, pool_extra=7)
     if sparse:
         case.update(topk=100, indices=_indices(case, 100))
-    o1, l1 = GpuRun(case)()
-    o2, l2 = GpuRun(_permute_pages(case))()
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(_permute_pages(case))()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_graph_replay_100(fused):
     case = synth.config_case(2, B=8)
-    run = GpuRun(case, fused=fused)
+    run = DecodeRun(case, fused=fused)
     o_ref, l_ref = run()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -26,7 +26,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity
+from gpu_util import DecodeRun, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,7 @@ def test_max_batch_plan_words(splits):
 @pytest.mark.parametrize("splits", [0, 2])
 def test_max_batch_parity(splits):
     case = _case(_max_batch_lens(), splits=splits)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -84,7 +84,7 @@ def test_max_batch_parity(splits):
 def test_max_splits_parity(fmt):
     # 20000 tokens: 313 tiles of 64 in 157 chunks of 2 (99 empty); 70 tokens: 2 chunks of 1
     case = _case((20000, 70, 0), Hq=8, Hkv=2, D=128, P=64, fmt=fmt, splits=256)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -95,21 +95,21 @@ def test_max_splits_parity(fmt):
                                      fmt=synth.KV_FP8_PAGE_HEAD, splits=3)])
 def test_max_query_rows_parity(kw):
     case = _case(**kw)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_mla_max_query_rows_parity():
     case = _mla_case((150, 9, 70), q_len=8)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_mla_max_splits_parity():
     case = _mla_case((5000, 3), G=16, splits=256)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -117,7 +117,7 @@ def test_mla_max_splits_parity():
 @pytest.mark.parametrize("P", [16, 256])
 def test_page_size_extremes_parity(P):
     case = _case((1, P - 1, P, P + 1, 5 * P + 3), Hq=16, Hkv=2, D=128, P=P)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
@@ -131,7 +131,7 @@ def _scale_q(case, k):
 def test_extreme_logits_parity(fmt):
     case = _case((900, 5, 2100), Hq=16, Hkv=2, D=128, P=16, fmt=fmt, splits=0)
     _scale_q(case, 20.0)
-    out, lse = GpuRun(case)(scale=1.0)
+    out, lse = DecodeRun(case)(scale=1.0)
     ref_out, ref_lse = oracle.decode(case, scale=1.0)
     assert np.max(np.abs(ref_lse)) > 500.0
     assert_parity(case, out, lse, ref_out, ref_lse)
@@ -165,7 +165,7 @@ def _mla_lse_bars(case, scale):
 def test_mla_extreme_logits_parity():
     case = _mla_case((900, 5, 2100), G=32, splits=0)
     _scale_q(case, 20.0)
-    out, lse = GpuRun(case)(scale=1.0)
+    out, lse = DecodeRun(case)(scale=1.0)
     ref_out, ref_lse = oracle.decode(case, scale=1.0)
     assert np.max(np.abs(ref_lse)) > 500.0
     assert_parity(case, out, ref_lse, ref_out, ref_lse)     # out; lse below

@@ -8,7 +8,7 @@ import pytest
 import oracle
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity
+from gpu_util import DecodeRun, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ SPEC_CASES = [
 @pytest.mark.parametrize("kw", SPEC_CASES)
 def test_spec_parity(kw):
     case = _spec(**kw)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert out.shape == ref_out.shape
     assert_parity(case, out, lse, ref_out, ref_lse)
@@ -51,8 +51,8 @@ def test_spec_parity(kw):
                                 dict(q_len=2, splits=3, lens=(1, 2, 65, 200))])
 def test_spec_fused_equals_separate(kw):
     case = _spec(**kw)
-    o1, l1 = GpuRun(case)()
-    o2, l2 = GpuRun(case, fused=True)()
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(case, fused=True)()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
@@ -69,7 +69,7 @@ def test_spec_draft_token_sees_exactly_its_prefix():
     page = case["block_table"][0, t // P]
     case["k_pool"][page, 0, t % P] = synth.f32_to_bf16_bits(u * 12.0)
     scale = 4.0 / np.sqrt(D)
-    out, lse = GpuRun(case)(scale=scale)
+    out, lse = DecodeRun(case)(scale=scale)
     ref_out, ref_lse = oracle.decode(case, scale=scale)
     assert_parity(case, out, lse, ref_out, ref_lse)
     from test_oracle import dense_kv
@@ -83,7 +83,7 @@ def test_spec_llama70b_shape_sampled():
     """The Llama-70B-like workload with two draft tokens per request (16 query rows per
     KV head: the MFMA columns are all used), balanced plan, sampled pairs."""
     case = synth.config_case(1, q_len=2)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     B, Hkv, G = case["B"], case["Hkv"], case["G"]
     pairs = np.zeros((B, Hkv), bool)
     pairs[[0, 13, 31], [0, 5, 7]] = True
@@ -106,7 +106,7 @@ def _mla_spec(q_len, lens, G=64, P=64, splits=0, seed=41):
                                 dict(q_len=4, lens=(5000, 3), G=32)])
 def test_spec_mla_parity(kw):
     case = _mla_spec(**kw)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert out.shape == ref_out.shape
     assert_parity(case, out, lse, ref_out, ref_lse)
@@ -117,6 +117,6 @@ def test_spec_mla_with_window_and_sinks():
     rng = np.random.default_rng(12)
     case["window"] = 200
     case["sinks"] = (rng.standard_normal(64) + 1.0).astype(np.float32)
-    out, lse = GpuRun(case)()
+    out, lse = DecodeRun(case)()
     ref_out, ref_lse = oracle.decode(case)
     assert_parity(case, out, lse, ref_out, ref_lse)

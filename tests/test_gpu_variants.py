@@ -10,7 +10,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import GpuRun, assert_parity
+from gpu_util import DecodeRun, assert_parity
 from test_gpu_decode import _case, _mla_case
 from test_oracle_variants import _indices
 
@@ -23,7 +23,7 @@ def _sinks(case, seed=3, loc=1.0):
 
 
 def _check(case, fused=False):
-    out, lse = GpuRun(case, fused=fused)()
+    out, lse = DecodeRun(case, fused=fused)()
     ref_out, ref_lse = oracle.decode(case)
     assert out.shape == ref_out.shape
     assert_parity(case, out, lse, ref_out, ref_lse)
@@ -102,8 +102,8 @@ def test_sinks_parity(kw):
 def test_sinks_fused_equals_separate(kw):
     case = _case(**kw)
     case["sinks"] = _sinks(case)
-    o1, l1 = GpuRun(case)()
-    o2, l2 = GpuRun(case, fused=True)()
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(case, fused=True)()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
@@ -135,7 +135,7 @@ def test_sinks_mla(splits):
 def test_sinks_mla_fused_equals_separate(splits):
     case = _mla_case((1000, 33, 0, 300), G=64, P=64, splits=splits)
     case["sinks"] = _sinks(case)
-    o1, l1 = GpuRun(case)()
+    o1, l1 = DecodeRun(case)()
     o2, l2 = _check(case, fused=True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
@@ -143,7 +143,7 @@ def test_sinks_mla_fused_equals_separate(splits):
 def test_window_mla_fused_equals_separate():
     case = _mla_case((1000, 33, 300), G=32, P=64)
     case["window"] = 200
-    o1, l1 = GpuRun(case)()
+    o1, l1 = DecodeRun(case)()
     o2, l2 = _check(case, fused=True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
@@ -153,7 +153,7 @@ def test_sparse_mla_fused_is_unsupported():
     case["topk"] = 64
     case["indices"] = _indices(case, 64)
     with pytest.raises(pb.PaDecodeError) as e:
-        GpuRun(case, fused=True)()
+        DecodeRun(case, fused=True)()
     assert e.value.status == pb.PA_ERR_UNSUPPORTED
 
 
@@ -203,7 +203,7 @@ def test_sparse_mla_needle():
     tok[528:] = synth.f32_to_bf16_bits(x[512:]).view(np.uint8)
     case.update(topk=topk, indices=idx)
     scale = 8.0 / math.sqrt(576)
-    out, lse = GpuRun(case)(scale=scale)
+    out, lse = DecodeRun(case)(scale=scale)
     ref_out, ref_lse = oracle.decode(case, scale=scale)
     assert_parity(case, out, lse, ref_out, ref_lse)
     v = oracle.mla656_unpack(tok)[:512]
