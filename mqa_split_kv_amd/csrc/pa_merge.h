@@ -9,6 +9,13 @@
 
 #include "pa_internal.h"
 
+// The fused combine's ordering (relaxed agent-scope atomics plus a wait for the stores,
+// below) relies on gfx950's cross-XCD coherence of agent-scope accesses; no other device
+// target is built.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "pa_merge.h: the fused-combine ordering is written for gfx950 only"
+#endif
+
 namespace pa {
 
 typedef __bf16 merge_bf16x4 __attribute__((ext_vector_type(4)));

@@ -10,7 +10,10 @@ Recipe (numpy PCG64; one generator per case, seeded by the caller):
      of the permutation, in order; unused block-table entries are 0
   3. q ~ N(0, 1) rounded to bf16 (round to nearest even), shape [B, Hq, D]
   4. K pool, then V pool ~ N(0, 1) (every slot, also padding slots and unused
-     pages), drawn page-chunk by page-chunk
+     pages), drawn in chunks of consecutive pages; chunk c of pool w (0 = K or the
+     MLA pool, 1 = V) has its own PCG64 stream seeded with SeedSequence((seed, w, c)),
+     so that chunks are drawn in parallel and the values do not depend on the thread
+     count
   5. bf16 pools: rounded to bf16.
      fp8 page-head pools: per (page, KV head) scale = max|x| / 448 over the page's
      P*D values (1 if the max is 0), code = e4m3(RNE(x / scale)) saturated to +-448;
@@ -22,6 +25,7 @@ Recipe (numpy PCG64; one generator per case, seeded by the caller):
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional, Sequence
 
@@ -94,8 +98,31 @@ def _normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(size=shape, dtype=np.float32)
 
 
-def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
-              page_chunk: int = 4096) -> dict:
+# values per pool chunk (one independent stream each)
+CHUNK_VALUES = 1 << 24
+
+
+def _chunk_rng(seed: int, which: int, chunk: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence((seed, which, chunk))))
+
+
+def _fill_chunks(num_pages: int, values_per_page: int, seed: int, which: int, fill) -> None:
+    """Call fill(rng, p0, p1) for every chunk [p0, p1) of pages, in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    per = max(1, CHUNK_VALUES // values_per_page)
+    chunks = [(c, p0, min(num_pages, p0 + per)) for c, p0 in enumerate(range(0, num_pages, per))]
+    workers = max(1, min(len(chunks), 16, os.cpu_count() or 1))
+    if workers == 1:
+        for c, p0, p1 in chunks:
+            fill(_chunk_rng(seed, which, c), p0, p1)
+        return
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(fill, _chunk_rng(seed, which, c), p0, p1) for c, p0, p1 in chunks]:
+            f.result()
+
+
+def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None) -> dict:
     """Draw one instance.  Returns a dict of numpy arrays plus shape fields.
 
     Keys: B, Hkv, G, D, Dv, page_size, num_pages, max_pages, s_page, s_head, s_tok
@@ -139,9 +166,9 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
     if spec.kv_format == KV_MLA656:
         assert Hkv == 1 and D == 576 and Dv == 512
         pool = np.empty((num_pages, P, MLA_TOKEN_BYTES), np.uint8)
-        for p0 in range(0, num_pages, page_chunk):
-            p1 = min(num_pages, p0 + page_chunk)
-            x = _normal_f32(rng, (p1 - p0, P, 576))
+
+        def fill_mla(crng, p0, p1):
+            x = _normal_f32(crng, (p1 - p0, P, 576))
             nope = x[..., :512].reshape(p1 - p0, P, 4, 128)
             amax = np.abs(nope).max(axis=-1)
             sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
@@ -150,6 +177,8 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
             pool[p0:p1, :, 0:512] = codes
             pool[p0:p1, :, 512:528] = sc.view(np.uint8).reshape(p1 - p0, P, 16)
             pool[p0:p1, :, 528:656] = rope.view(np.uint8).reshape(p1 - p0, P, 128)
+
+        _fill_chunks(num_pages, P * 576, seed, 0, fill_mla)
         case.update(k_pool=pool, v_pool=None, s_page=P * MLA_TOKEN_BYTES, s_head=0,
                     s_tok=MLA_TOKEN_BYTES)
         return case
@@ -157,12 +186,12 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
     assert D == Dv
     fp8 = spec.kv_format == KV_FP8_PAGE_HEAD
     pools, scales = [], []
-    for _which in ("k", "v"):
+    for which in (0, 1):
         pool = np.empty((num_pages, Hkv, P, D), np.uint8 if fp8 else np.uint16)
         sc_all = np.empty((num_pages, Hkv), np.float32) if fp8 else None
-        for p0 in range(0, num_pages, page_chunk):
-            p1 = min(num_pages, p0 + page_chunk)
-            x = _normal_f32(rng, (p1 - p0, Hkv, P, D))
+
+        def fill_kv(crng, p0, p1, pool=pool, sc_all=sc_all):
+            x = _normal_f32(crng, (p1 - p0, Hkv, P, D))
             if fp8:
                 amax = np.abs(x).max(axis=(2, 3))
                 sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
@@ -170,6 +199,8 @@ def make_case(spec: CaseSpec, seed: int, scale: Optional[float] = None,
                 sc_all[p0:p1] = sc
             else:
                 pool[p0:p1] = f32_to_bf16_bits(x)
+
+        _fill_chunks(num_pages, Hkv * P * D, seed, which, fill_kv)
         pools.append(pool)
         scales.append(sc_all)
     case.update(k_pool=pools[0], v_pool=pools[1], k_scale=scales[0], v_scale=scales[1])

@@ -4,8 +4,8 @@ Plan buffers must match the oracle's partition definitions word for word; output
 must match the oracle element by element within |out diff| <= 1e-2 * max|V| and
 |lse diff| <= 1e-3, on seeded synthetic inputs: small cases that span several
 tiles and ragged tails, the tiny / HD64 workloads at full size, the Llama-70B-like
-and ragged FP8 workloads at full size in the balanced-plan launch configuration
-the benchmark times (all rows, or sampled (request, KV head) pairs), and
+ragged FP8 and MLA workloads at full size, every row, in the balanced-plan launch
+configuration the benchmark times, and
 boundary "needle" cases where a single mis-gathered token moves the output by O(1).
 """
 import math
@@ -19,7 +19,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import DecodeRun, assert_parity, to_device
+from gpu_util import DecodeRun, assert_parity, to_device, workload, workload_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -118,27 +118,20 @@ def test_hd64_config(B):
 
 
 def test_llama70b_config_full():
-    case = synth.config_case(1)
+    case = workload(1)
     out, lse = DecodeRun(case)()
-    ref_out, ref_lse = oracle.decode(case)
+    ref_out, ref_lse = workload_ref(1)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
-def test_ragged_fp8_config_sampled():
-    case = synth.config_case(3)
+def test_ragged_fp8_config_full():
+    """Every (request, KV head) row of the ragged FP8 workload (64 requests, lengths
+    256 .. 131072) in the balanced-plan launch the benchmark times."""
+    case = workload(3)
     run = DecodeRun(case)
     out, lse = run()
-    B, Hkv, G = case["B"], case["Hkv"], case["G"]
-    rng = np.random.default_rng(0)
-    L = case["seq_lens"]
-    bs = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + list(rng.choice(B, 6, replace=False))))
-    pairs = np.zeros((B, Hkv), bool)
-    for b in bs:
-        pairs[b, rng.choice(Hkv, 2, replace=False)] = True
-    ref_out, ref_lse = oracle.decode(case, pairs=pairs)
-    rows = np.repeat(pairs, G, axis=1)
-    assert_parity(case, out, lse, ref_out, ref_lse, rows=rows)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    ref_out, ref_lse = workload_ref(3)
+    assert_parity(case, out, lse, ref_out, ref_lse)
     # the plan it ran is the balanced partition of these lengths
     words = run.plan_words()
     ref = oplan.plan_words(list(case["seq_lens"]), 0, pb.pa_decode_num_parts(run.desc))
@@ -276,17 +269,12 @@ def test_mla_small_parity(kw):
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
-def test_mla_config_full_sampled():
-    case = synth.config_case(4)
-    run = DecodeRun(case)
-    out, lse = run()
-    B = case["B"]
-    pairs = np.zeros((B, 1), bool)
-    pairs[[0, 17, 40, B - 1], 0] = True
-    ref_out, ref_lse = oracle.decode(case, pairs=pairs)
-    rows = np.repeat(pairs, case["G"], axis=1)
-    assert_parity(case, out, lse, ref_out, ref_lse, rows=rows)
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+def test_mla_config_full():
+    """Every row of the MLA workload (64 requests x 128 heads, 8192 tokens each)."""
+    case = workload(4)
+    out, lse = DecodeRun(case)()
+    ref_out, ref_lse = workload_ref(4)
+    assert_parity(case, out, lse, ref_out, ref_lse)
 
 
 def test_mla_q_dynamic_range():

@@ -17,7 +17,7 @@ from oracle import plan as oplan
 from mqa_split_kv_amd import binding as pb
 from mqa_split_kv_amd import synth
 
-from gpu_util import DecodeRun, assert_parity, bf16_bits_to_f64, to_device
+from gpu_util import DecodeRun, assert_parity, bf16_bits_to_f64, to_device, workload, workload_ref
 from test_gpu_decode import _case, _mla_case
 
 pytestmark = pytest.mark.gpu
@@ -107,37 +107,31 @@ def test_fused_mla_equals_separate_and_oracle(kw):
     _check_counters_zero(run)
 
 
-def test_fused_mla_config_sampled():
-    case = synth.config_case(4)
+def test_fused_mla_config():
+    case = workload(4)
     o_sep, l_sep = DecodeRun(case)()
     run = DecodeRun(case, fused=True)
     o_fu, l_fu = run()
     assert np.array_equal(o_fu, o_sep) and np.array_equal(l_fu, l_sep)
+    ref_out, ref_lse = workload_ref(4)
+    assert_parity(case, o_fu, l_fu, ref_out, ref_lse)
     _check_counters_zero(run)
 
 
-def test_fused_ragged_fp8_config_sampled():
-    case = synth.config_case(3)
+def test_fused_ragged_fp8_config():
+    case = workload(3)
     run = DecodeRun(case, fused=True)
     out, lse = run()
-    B, Hkv, G = case["B"], case["Hkv"], case["G"]
-    rng = np.random.default_rng(7)
-    L = case["seq_lens"]
-    bs = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + list(rng.choice(B, 4, replace=False))))
-    pairs = np.zeros((B, Hkv), bool)
-    for b in bs:
-        pairs[b, rng.choice(Hkv, 2, replace=False)] = True
-    ref_out, ref_lse = oracle.decode(case, pairs=pairs)
-    assert_parity(case, out, lse, ref_out, ref_lse, rows=np.repeat(pairs, G, axis=1))
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    ref_out, ref_lse = workload_ref(3)
+    assert_parity(case, out, lse, ref_out, ref_lse)
     _check_counters_zero(run)
 
 
 @pytest.mark.parametrize("B", [1, 8])
 def test_fused_hd64_config(B):
-    case = synth.config_case(2, B=B)
+    case = workload(2, B=B)
     out, lse = DecodeRun(case, fused=True)()
-    ref_out, ref_lse = oracle.decode(case)
+    ref_out, ref_lse = workload_ref(2, B=B)
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 

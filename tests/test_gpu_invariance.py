@@ -5,6 +5,8 @@ page sits in the pool cannot change a single bit of the result; XQA article, sec
 * page-table permutation: the same logical KV moved to other physical pages (pool rows
   and per-page scales permuted, block table remapped) gives bit-identical out and lse,
   for bf16 (HND and NHD strides), fp8 page-head and MLA-656, dense and sparse;
+* page-size repacking: the same tokens stored with another page size (other pages,
+  garbage elsewhere) give bit-identical out and lse (bf16 HND / NHD, HD64, MLA-656);
 * graph replay x100: one captured step (run + combine) replayed 100 times, with eager
   work between replays, reproduces the eager result bit for bit every time.
 """
@@ -60,6 +62,33 @@ def test_mla_page_permutation_bit_identical(sparse):
         case.update(topk=100, indices=_indices(case, 100))
     o1, l1 = DecodeRun(case)()
     o2, l2 = DecodeRun(_permute_pages(case))()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+REPACK_CASES = [
+    ("bf16 16->64", dict(Hq=32, Hkv=8, D=128, P=16, lens=(2000, 33, 4097), splits=0), 64),
+    ("bf16 NHD 64->16", dict(layout="NHD", Hq=16, Hkv=2, D=64, P=64, lens=(129, 7, 640), splits=3), 16),
+    ("hd64 256->32", dict(Hq=32, Hkv=4, D=64, P=256, lens=(1536, 700), splits=8), 32),
+]
+
+
+@pytest.mark.parametrize("name,kw,P_new", REPACK_CASES, ids=[c[0] for c in REPACK_CASES])
+def test_page_size_repacking_bit_identical(name, kw, P_new):
+    """The same tokens stored with another page size give bit-identical out and lse: the
+    kernels' arithmetic follows token positions, pages only locate the bytes."""
+    from repack import repack
+    case = _case(**kw)
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(repack(case, P_new, seed=3))()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("P,P_new", [(64, 16), (16, 256)])
+def test_mla_page_size_repacking_bit_identical(P, P_new):
+    from repack import repack
+    case = _mla_case((1000, 33, 300), G=64, P=P)
+    o1, l1 = DecodeRun(case)()
+    o2, l2 = DecodeRun(repack(case, P_new, seed=4))()
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 

@@ -4,8 +4,8 @@
   logsumexp) on contiguous K/V gathered with numpy fancy indexing;
 * element codecs against torch's own bf16 / float8_e4m3fn conversions;
 * closed forms (one token, identical keys, zero query, one dominant logit);
-* invariances (page relocation, HND vs NHD, garbage in unused slots, GQA vs
-  expanded MHA, split + merge vs whole);
+* invariances (page relocation, page-size repacking, HND vs NHD, garbage in unused
+  slots, other heads' data, GQA vs expanded MHA, split + merge vs whole);
 * the worked rescale example of the pipelining page (tests/golden).
 """
 import json
@@ -284,6 +284,70 @@ def test_garbage_in_unused_slots_is_ignored(fmt):
         np.copyto(pool, junk, where=np.broadcast_to(mask, pool.shape))
     out1, lse1 = oracle.decode(case)
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+@pytest.mark.parametrize("fmt,layout,P,P_new", [(synth.KV_BF16, "HND", 16, 64),
+                                                 (synth.KV_BF16, "NHD", 64, 16),
+                                                 (synth.KV_BF16, "HND", 32, 256),
+                                                 (synth.KV_MLA656, "HND", 64, 16),
+                                                 (synth.KV_MLA656, "HND", 16, 256)])
+def test_page_size_repacking_invariance(fmt, layout, P, P_new):
+    """The same tokens stored with another page size (and other physical pages, and
+    garbage elsewhere) give bit-identical results: the definition sums over token
+    positions, pages only say where a token's bytes are."""
+    from repack import repack
+    case = small_case(fmt=fmt, layout=layout, P=P, lens=(40, 300, 7, 1), B=4, D=128)
+    out0, lse0 = oracle.decode(case)
+    moved = repack(case, P_new, seed=P_new)
+    out1, lse1 = oracle.decode(moved)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+    # and the result is not vacuous: the library path agrees on the repacked cache
+    ref_out, ref_lse = library_attention(moved)
+    np.testing.assert_allclose(out1, ref_out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse1, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8_PAGE_HEAD])
+def test_other_heads_data_leaves_this_head_unchanged(fmt):
+    """Changing the K/V of every other KV head and the queries of their groups leaves
+    the rows of KV head h bit-identical, and changes the rows of the others."""
+    case = small_case(fmt=fmt, Hq=16, Hkv=4, D=64, lens=(40, 100, 7))
+    out0, lse0 = oracle.decode(case)
+    G, Hkv, h = case["G"], case["Hkv"], 2
+    other = [x for x in range(Hkv) if x != h]
+    rng = np.random.default_rng(3)
+    mod = dict(case)
+    for key in ("k_pool", "v_pool"):
+        a = case[key].copy()
+        sel = a[:, other]                                     # HND: [page][head][P][D]
+        a[:, other] = np.roll(sel, 1, axis=2)                 # other tokens' bytes
+        mod[key] = a
+    if fmt == synth.KV_FP8_PAGE_HEAD:
+        for key in ("k_scale", "v_scale"):
+            a = case[key].copy()
+            a[:, other] *= np.float32(1.5)
+            mod[key] = a
+    q = case["q"].copy()
+    rows = np.concatenate([np.arange(o * G, (o + 1) * G) for o in other])
+    q[:, rows] = synth.f32_to_bf16_bits(rng.standard_normal(q[:, rows].shape).astype(np.float32))
+    mod["q"] = q
+    out1, lse1 = oracle.decode(mod)
+    mine = slice(h * G, (h + 1) * G)
+    assert np.array_equal(out0[:, mine], out1[:, mine]) and np.array_equal(lse0[:, mine], lse1[:, mine])
+    assert not np.array_equal(lse0[:, rows], lse1[:, rows])
+
+
+def test_mla_other_query_heads_leave_this_head_unchanged():
+    """MQA: each query head's row depends on its own query only."""
+    case = small_case(fmt=synth.KV_MLA656, Hq=32, P=16, lens=(20, 47, 3))
+    out0, lse0 = oracle.decode(case)
+    q = case["q"].copy()
+    rng = np.random.default_rng(4)
+    q[:, 1:] = synth.f32_to_bf16_bits(rng.standard_normal(q[:, 1:].shape).astype(np.float32))
+    mod = dict(case, q=q)
+    out1, lse1 = oracle.decode(mod)
+    assert np.array_equal(out0[:, 0], out1[:, 0]) and np.array_equal(lse0[:, 0], lse1[:, 0])
+    assert not np.array_equal(lse0[:, 1:], lse1[:, 1:])
 
 
 def test_grouped_heads_equal_independent_mha():
