@@ -219,6 +219,28 @@ pa_status pa_kv_append(const pa_decode_desc *desc, int32_t n_new, const void *k_
                        const void *v_new, const int32_t *block_table, const int32_t *seq_lens,
                        void *k_pool, void *v_pool, float *k_scale, float *v_scale, void *stream);
 
+/*
+ * No-allocation decode step, for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc):
+ * pa_decode_plan + pa_decode_run + pa_decode_combine in one call, with the plan and the
+ * chunk partials in a buffer the library holds in device memory instead of caller
+ * buffers: PA_NOALLOC_SCRATCH_BYTES per device, reserved when the library is loaded on
+ * that device and kept until the process ends.  Arguments as for pa_decode_run (flags,
+ * q_len, window, topk and sinks included); the result is bit-identical to the three-call
+ * sequence.  Every call on one device shares that buffer and leaves its contents there:
+ * calls that overlap on one device (other streams, other threads) race on it, so the
+ * caller must order them.  The plan is rebuilt on every call (the plan kernel also
+ * clears the fused-combine counters it holds).  PA_ERR_SIZE: this desc's plan (rounded
+ * up to 256 bytes) and partials need more than PA_NOALLOC_SCRATCH_BYTES; nothing is
+ * enqueued.  No allocation, free or synchronisation.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(const pa_decode_desc *desc, const void *q, const void *k_pool,
+                            const void *v_pool, const float *k_scale, const float *v_scale,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            const int32_t *indices, const float *sinks, float scale, void *out,
+                            float *lse, void *stream);
+
 /* Number of workgroups along the part axis that pa_decode_run launches for `desc`
    on the current device (B * num_splits, or the balanced part count). */
 pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts);

@@ -20,7 +20,8 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_SIZE, PA_ERR_DEVICE = range(5)
 PA_KV_BF16, PA_KV_FP8_E4M3_PAGE_HEAD, PA_KV_MLA656 = range(3)
 PA_FLAG_FUSED_COMBINE = 1
 EXPORTS = ("pa_decode_plan", "pa_decode_run", "pa_decode_combine", "pa_kv_append",
-           "pa_decode_num_parts", "pa_status_string")
+           "pa_decode_noalloc", "pa_decode_num_parts", "pa_status_string")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PaDecodeDesc(ctypes.Structure):
@@ -56,12 +57,14 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_run.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                     vp, vp, vp, vp]
         L.pa_decode_combine.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+        L.pa_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                        vp, vp, vp]
         L.pa_kv_append.argtypes = [dp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_decode_num_parts.argtypes = [dp, ctypes.POINTER(ctypes.c_int32)]
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
         for f in ("pa_decode_plan", "pa_decode_run", "pa_decode_combine", "pa_kv_append",
-                  "pa_decode_num_parts"):
+                  "pa_decode_noalloc", "pa_decode_num_parts"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -129,6 +132,16 @@ def pa_decode_combine(desc: PaDecodeDesc, plan, workspace, out, lse, stream=None
     st = lib().pa_decode_combine(ctypes.byref(desc), _p(plan), _p(workspace), _p(sinks), _p(out),
                                  _p(lse), _stream(stream))
     _check("pa_decode_combine", st)
+
+
+def pa_decode_noalloc(desc: PaDecodeDesc, q, k_pool, v_pool, k_scale, v_scale, block_table,
+                      seq_lens, scale: float, out, lse, stream=None, indices=None, sinks=None):
+    """Plan + decode + combine with the library's own device buffer (no allocation)."""
+    st = lib().pa_decode_noalloc(ctypes.byref(desc), _p(q), _p(k_pool), _p(v_pool), _p(k_scale),
+                                 _p(v_scale), _p(block_table), _p(seq_lens), _p(indices),
+                                 _p(sinks), ctypes.c_float(scale), _p(out), _p(lse),
+                                 _stream(stream))
+    _check("pa_decode_noalloc", st)
 
 
 def pa_kv_append(desc: PaDecodeDesc, n_new: int, k_new, v_new, block_table, seq_lens, k_pool,

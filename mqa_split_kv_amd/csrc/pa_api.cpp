@@ -123,6 +123,125 @@ pa_status layout_for(const pa_decode_desc *d, PlanLayout *L)
     return PA_OK;
 }
 
+// Device buffer of the no-allocation entry point (plan words, then the partials): one
+// copy per device, reserved when the library is loaded there and kept until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it is only a
+// handle); it uses the device address that hipGetSymbolAddress returns, kept per device.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+
+// Device address of this device's scratch (looked up on the first call on the device).
+pa_status scratch_base(uint8_t **base)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_DEVICE;
+    uintptr_t v = g_scratch[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return PA_ERR_DEVICE;
+        v = (uintptr_t)ptr;
+        g_scratch[dev].store(v, std::memory_order_release);
+    }
+    *base = (uint8_t *)v;
+    return PA_OK;
+}
+
+// Pointer and value checks of a decode launch (the desc is already checked).
+pa_status check_run_args(const pa_decode_desc *desc, const void *q, const void *k_pool,
+                         const void *v_pool, const float *k_scale, const float *v_scale,
+                         const int32_t *block_table, const int32_t *seq_lens,
+                         const int32_t *indices, const float *sinks, float scale, void *out,
+                         float *lse)
+{
+    if (!q || !k_pool || !block_table || !seq_lens || !out || !lse) return PA_ERR_INVALID;
+    if ((desc->topk > 0) != (indices != nullptr)) return PA_ERR_INVALID;
+    if (((uintptr_t)indices & 3) || ((uintptr_t)sinks & 3)) return PA_ERR_INVALID;
+    const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
+    const bool mla = desc->kv_format == PA_KV_MLA656;
+    if (mla ? v_pool != nullptr : !v_pool) return PA_ERR_INVALID;
+    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_pool) || (!mla && !aligned16(v_pool)) || !aligned16(out) ||
+        ((uintptr_t)lse & 3) || ((uintptr_t)block_table & 3) || ((uintptr_t)seq_lens & 3))
+        return PA_ERR_INVALID;
+    if (!isfinite(scale)) return PA_ERR_INVALID;
+    return PA_OK;
+}
+
+// Enqueue the decode kernel for validated arguments.
+pa_status launch_run(const pa_decode_desc *desc, const PlanLayout &L, void *plan, const void *q,
+                     const void *k_pool, const void *v_pool, const float *k_scale,
+                     const float *v_scale, const int32_t *block_table, const int32_t *seq_lens,
+                     const int32_t *indices, const float *sinks, float scale, void *out,
+                     float *lse, void *workspace, hipStream_t stream)
+{
+    pa::DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    const int64_t eb = elem_bytes(desc->kv_format);
+    a.q = (const uint16_t *)q;
+    a.k_pool = (const uint8_t *)k_pool;
+    a.v_pool = (const uint8_t *)v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.plan = (const int32_t *)plan;
+    a.out = (uint16_t *)out;
+    a.lse = lse;
+    a.ws_o = (float *)workspace;
+    a.ws_lse = workspace ? (float *)((uint8_t *)workspace +
+                                     pa::ws_o_bytes(L.max_items,
+                                                    desc->q_len * desc->Hkv * desc->G, desc->Dv))
+                         : nullptr;
+    a.seq_lens = seq_lens;
+    a.indices = indices;
+    a.sinks = sinks;
+    a.q_len = desc->q_len;
+    a.window = desc->window;
+    a.topk = desc->topk;
+    a.s_page_b = desc->s_page * eb;
+    a.s_head_b = desc->s_head * eb;
+    a.s_tok_b = desc->s_tok * eb;
+    a.B = desc->B;
+    a.Hkv = desc->Hkv;
+    a.G = desc->G;
+    a.D = desc->D;
+    a.Dv = desc->Dv;
+    a.max_pages = desc->max_pages_per_seq;
+    a.page_shift = __builtin_ctz((unsigned)desc->page_size);
+    a.num_parts = L.num_parts;
+    a.part_begin_off = L.part_begin_off;
+    a.items_off = L.items_off;
+    a.chunk_off_off = L.chunk_off_off;
+    a.fixed_splits = desc->num_splits > 0 ? desc->num_splits : 0;
+    a.counters = (desc->flags & PA_FLAG_FUSED_COMBINE) && desc->num_splits != 1
+                     ? (int32_t *)plan + L.counters_off
+                     : nullptr;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)desc->D);
+    a.scale_log2 = sc * 1.4426950408889634f;
+    a.kv_format = desc->kv_format;
+    const hipError_t e = desc->kv_format == PA_KV_MLA656 ? pa::launch_mla(a, stream)
+                                                         : pa::launch_decode(a, stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_DEVICE;
+}
+
+// Enqueue the combine kernel (nothing for one chunk per request or a fused run).
+pa_status launch_combine_for(const pa_decode_desc *desc, const PlanLayout &L, const void *plan,
+                             const void *workspace, const float *sinks, void *out, float *lse,
+                             hipStream_t stream)
+{
+    if (desc->num_splits == 1 || (desc->flags & PA_FLAG_FUSED_COMBINE)) return PA_OK;
+    const float *ws_o = (const float *)workspace;
+    const float *ws_lse = (const float *)((const uint8_t *)workspace +
+                                          pa::ws_o_bytes(L.max_items,
+                                                         desc->q_len * desc->Hkv * desc->G,
+                                                         desc->Dv));
+    if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, sinks, (uint16_t *)out, lse, desc->B,
+                           desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
+                           desc->num_splits > 0 ? desc->num_splits : 0, stream) != hipSuccess)
+        return PA_ERR_DEVICE;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,72 +325,18 @@ pa_status pa_decode_run(const pa_decode_desc *desc, void *plan, const void *q,
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK) return st;
-    if (!plan || !q || !k_pool || !block_table || !seq_lens || !out || !lse)
-        return PA_ERR_INVALID;
-    if ((desc->topk > 0) != (indices != nullptr)) return PA_ERR_INVALID;
-    if (((uintptr_t)indices & 3) || ((uintptr_t)sinks & 3)) return PA_ERR_INVALID;
-    const bool fp8 = desc->kv_format == PA_KV_FP8_E4M3_PAGE_HEAD;
-    const bool mla = desc->kv_format == PA_KV_MLA656;
-    if (mla ? v_pool != nullptr : !v_pool) return PA_ERR_INVALID;
-    if (fp8 && (!k_scale || !v_scale)) return PA_ERR_INVALID;
-    if (!aligned16(q) || !aligned16(k_pool) || (!mla && !aligned16(v_pool)) || !aligned16(out) ||
-        ((uintptr_t)lse & 3) || ((uintptr_t)plan & 3) || ((uintptr_t)block_table & 3))
-        return PA_ERR_INVALID;
+    if (!plan) return PA_ERR_INVALID;
+    st = check_run_args(desc, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, indices,
+                        sinks, scale, out, lse);
+    if (st != PA_OK) return st;
+    if (((uintptr_t)plan & 3)) return PA_ERR_INVALID;
+    const bool needs_ws = !(desc->num_splits == 1);
+    if (needs_ws && (!workspace || !aligned16(workspace))) return PA_ERR_INVALID;
     PlanLayout L;
     st = layout_for(desc, &L);
     if (st != PA_OK) return st;
-    const bool needs_ws = !(desc->num_splits == 1);
-    if (needs_ws && (!workspace || !aligned16(workspace))) return PA_ERR_INVALID;
-    if (!isfinite(scale)) return PA_ERR_INVALID;
-
-    pa::DecodeArgs a;
-    memset(&a, 0, sizeof a);
-    const int64_t eb = elem_bytes(desc->kv_format);
-    a.q = (const uint16_t *)q;
-    a.k_pool = (const uint8_t *)k_pool;
-    a.v_pool = (const uint8_t *)v_pool;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.plan = (const int32_t *)plan;
-    a.out = (uint16_t *)out;
-    a.lse = lse;
-    a.ws_o = (float *)workspace;
-    a.ws_lse = workspace ? (float *)((uint8_t *)workspace +
-                                     pa::ws_o_bytes(L.max_items,
-                                                    desc->q_len * desc->Hkv * desc->G, desc->Dv))
-                         : nullptr;
-    a.seq_lens = seq_lens;
-    a.indices = indices;
-    a.sinks = sinks;
-    a.q_len = desc->q_len;
-    a.window = desc->window;
-    a.topk = desc->topk;
-    a.s_page_b = desc->s_page * eb;
-    a.s_head_b = desc->s_head * eb;
-    a.s_tok_b = desc->s_tok * eb;
-    a.B = desc->B;
-    a.Hkv = desc->Hkv;
-    a.G = desc->G;
-    a.D = desc->D;
-    a.Dv = desc->Dv;
-    a.max_pages = desc->max_pages_per_seq;
-    a.page_shift = __builtin_ctz((unsigned)desc->page_size);
-    a.num_parts = L.num_parts;
-    a.part_begin_off = L.part_begin_off;
-    a.items_off = L.items_off;
-    a.chunk_off_off = L.chunk_off_off;
-    a.fixed_splits = desc->num_splits > 0 ? desc->num_splits : 0;
-    a.counters = (desc->flags & PA_FLAG_FUSED_COMBINE) && desc->num_splits != 1
-                     ? (int32_t *)plan + L.counters_off
-                     : nullptr;
-    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)desc->D);
-    a.scale_log2 = sc * 1.4426950408889634f;
-    a.kv_format = desc->kv_format;
-    const hipError_t e = mla ? pa::launch_mla(a, (hipStream_t)stream)
-                             : pa::launch_decode(a, (hipStream_t)stream);
-    if (e != hipSuccess) return PA_ERR_DEVICE;
-    return PA_OK;
+    return launch_run(desc, L, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                      indices, sinks, scale, out, lse, workspace, (hipStream_t)stream);
 }
 
 pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const void *workspace,
@@ -288,16 +353,36 @@ pa_status pa_decode_combine(const pa_decode_desc *desc, const void *plan, const 
     PlanLayout L;
     st = layout_for(desc, &L);
     if (st != PA_OK) return st;
-    const float *ws_o = (const float *)workspace;
-    const float *ws_lse = (const float *)((const uint8_t *)workspace +
-                                          pa::ws_o_bytes(L.max_items,
-                                                         desc->q_len * desc->Hkv * desc->G,
-                                                         desc->Dv));
-    if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, sinks, (uint16_t *)out, lse, desc->B,
-                           desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
-                           desc->num_splits > 0 ? desc->num_splits : 0, (hipStream_t)stream) != hipSuccess)
-        return PA_ERR_DEVICE;
-    return PA_OK;
+    return launch_combine_for(desc, L, plan, workspace, sinks, out, lse, (hipStream_t)stream);
+}
+
+pa_status pa_decode_noalloc(const pa_decode_desc *desc, const void *q, const void *k_pool,
+                            const void *v_pool, const float *k_scale, const float *v_scale,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            const int32_t *indices, const float *sinks, float scale, void *out,
+                            float *lse, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK) return st;
+    st = check_run_args(desc, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, indices,
+                        sinks, scale, out, lse);
+    if (st != PA_OK) return st;
+    PlanLayout L;
+    st = layout_for(desc, &L);
+    if (st != PA_OK) return st;
+    const size_t plan_bytes = (L.words * 4 + 255) & ~(size_t)255;
+    const size_t ws = pa::ws_bytes(L.max_items, desc->q_len * desc->Hkv * desc->G, desc->Dv);
+    if (plan_bytes + ws > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SIZE;
+    uint8_t *base = nullptr;
+    st = scratch_base(&base);
+    if (st != PA_OK) return st;
+    void *plan = base, *workspace = base + plan_bytes;
+    const hipStream_t s = (hipStream_t)stream;
+    if (pa::launch_plan(seq_lens, (int32_t *)plan, L, desc, s) != hipSuccess) return PA_ERR_DEVICE;
+    st = launch_run(desc, L, plan, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens,
+                    indices, sinks, scale, out, lse, workspace, s);
+    if (st != PA_OK) return st;
+    return launch_combine_for(desc, L, plan, workspace, sinks, out, lse, s);
 }
 
 }  // extern "C"

@@ -179,3 +179,35 @@ def test_append_rejects_bad_arguments_on_host():
     dm = _desc(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=656, s_page=656 * 16)
     assert L.pa_kv_append(ctypes.byref(dm), 1, *[p(base)] * 6, None, None,
                           None) == pb.PA_ERR_INVALID                                 # v_new given
+
+
+def _noalloc_status(desc, ptr=0x100000):
+    """pa_decode_noalloc with placeholder (never dereferenced) device addresses."""
+    p = ctypes.c_void_p(ptr)
+    mla = desc.kv_format == pb.PA_KV_MLA656
+    return pb.lib().pa_decode_noalloc(ctypes.byref(desc), p, p, None if mla else p, None, None, p,
+                                      p, None, None, ctypes.c_float(0.0), p, p, None)
+
+
+def test_noalloc_rejects_more_than_its_buffer():
+    # MLA, 8 draft tokens x 128 heads, 4 fixed splits of 8 requests: 32 chunk partials of
+    # 1024 rows x 512 fp32 = 64 MiB, plus their lse and the plan: beyond the buffer
+    desc = _desc(B=8, kv_format=pb.PA_KV_MLA656, Hkv=1, G=128, D=576, Dv=512, s_tok=656,
+                 s_page=656 * 16, q_len=8, num_splits=4)
+    _, pbytes, wbytes = _plan_status(desc)
+    assert ((pbytes + 255) // 256 * 256) + wbytes > pb.NOALLOC_SCRATCH_BYTES
+    assert _noalloc_status(desc) == pb.PA_ERR_SIZE
+    # 3 splits fit (the call then needs the device: no GPU here)
+    small = _desc(B=8, kv_format=pb.PA_KV_MLA656, Hkv=1, G=128, D=576, Dv=512, s_tok=656,
+                  s_page=656 * 16, q_len=8, num_splits=3)
+    _, pbytes, wbytes = _plan_status(small)
+    assert ((pbytes + 255) // 256 * 256) + wbytes <= pb.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validates_arguments():
+    assert _noalloc_status(_desc(B=0)) == pb.PA_ERR_INVALID
+    assert _noalloc_status(_desc(), ptr=0x100008) == pb.PA_ERR_INVALID      # misaligned
+    p = ctypes.c_void_p(0x100000)
+    st = pb.lib().pa_decode_noalloc(ctypes.byref(_desc()), None, p, p, None, None, p, p, None,
+                                    None, ctypes.c_float(0.0), p, p, None)
+    assert st == pb.PA_ERR_INVALID                                            # no q
