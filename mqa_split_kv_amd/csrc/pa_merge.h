@@ -146,7 +146,7 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
 }
 
 // Fused combine, called by every thread of a workgroup once it has processed all its
-// items [ib, ie) (row group rg: query heads [hq0, hq0 + nrows) of every query token;
+// items [ib, ie) (kUnits: the merge's units per thread and pass, as in merge_rows) (row group rg: query heads [hq0, hq0 + nrows) of every query token;
 // `arrivals` workgroups write partials per chunk of the row group).  The partials were
 // written with store_shared; each thread waits until its stores are complete, the
 // workgroup meets, and one thread counts each of the workgroup's partial chunks in with a
@@ -155,6 +155,7 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
 // it observed), merges that request, and returns its counter to zero.  Then requests with no chunk at all (length 0 under the
 // balanced rule) get out = 0, lse = -inf (or the sink) from workgroup part = b mod
 // num_parts.
+template <int kUnits = 4>
 __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *plan, int part,
                                           int ib, int ie, int rg, int n_rowgroups, int hq0,
                                           int nrows, int arrivals, int *s_flag)
@@ -178,7 +179,7 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
                       n * arrivals - 1;
         __syncthreads();
         if (*s_flag) {
-            merge_rows<4, true>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
+            merge_rows<kUnits, true>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
                                 nrows, threadIdx.x, blockDim.x);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

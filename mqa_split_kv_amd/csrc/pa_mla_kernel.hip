@@ -3,9 +3,13 @@
 //
 // Token layout (FlashMLA walk-through, section 数据加载, byte-layout table): 512 e4m3
 // codes, 4 fp32 scales (one per 128 codes), 64 bf16 rope values.  The key is the 576
-// dequantised values, the value is their first 512 (V shares the latent with K).
+// dequantised values, the value is their first 512 (V shares the latent with K).  Both
+// products run as bf16 MFMAs with fp32 accumulation, as the walk-through's kernel does
+// (same section): the codes are converted to bf16 exactly (every e4m3 value is a bf16
+// value) and the per-token tile scales are applied in fp32, to the score partials of each
+// 128-dim tile and to the probabilities of each 128-dim value tile.
 //
-// One workgroup (8 waves, two per SIMD) = one (part, group of 64 query rows); it walks
+// One workgroup (12 waves, three per SIMD) = one (part, group of 64 query rows); it walks
 // the part's items.  Query rows are (draft token qi, head g) pairs, row qi * G + g, so with
 // several query tokens per request (a linear speculative draft) each block of 16 rows
 // shares one draft token and its causal limit L - q_len + qi + 1.  The two head groups of a
@@ -14,61 +18,60 @@
 // between two 64-head CTAs through a cluster, section 计算环节一; here the L2 of the XCD
 // plays that role).
 //
-// Waves hg and hg + 4 share a SIMD, with two roles (the FlashMLA walk-through splits a
-// tile's work over two warpgroups, section 计算环节二; here the split is by operation):
-//   * score wave hg (Q of head block hg resident) computes S^T[32 tok x 16 heads] = K . Q^T;
-//     in iteration i it runs tile i+1's MFMAs and, between them, tile i's softmax, and hands
-//     P^T of tile i to the value waves through LDS;
+// Waves hg, hg + 4 and hg + 8 share a SIMD (the FlashMLA walk-through splits a tile's work
+// over two warpgroups, section 计算环节二; here the split is by operation and by tokens):
+//   * score waves (hg, sb), sb = 0, 1: Q of head block hg resident (bf16, 72 registers);
+//     wave sb computes S^T = K . Q^T for the 16 tokens of row block sb of each 32-token
+//     tile, in iteration i the MFMAs of tile i+1 with tile i's softmax between them.  The
+//     two halves of a tile agree on one running maximum: each publishes its half's
+//     per-head maximum through LDS one iteration ahead, and both move the reference
+//     identically; each keeps its own partial row sum, added at the end of the item;
 //   * value wave hg (O^T of value dims 128 hg .. +127 for all 64 heads resident, 128
 //     registers) runs O^T += V^T . P^T of tile i-1 in iteration i: each V^T operand is read
 //     and converted once and feeds the 4 head blocks' MFMAs.
-// Two waves per SIMD let one wave's conversions, softmax and waits run under the other's
-// matrix work; the score wave also overlaps its own softmax with its next tile's MFMAs (a
-// wave's dependent VALU chains and its LDS and barrier waits otherwise stall its own MFMA
-// issue).
+// A wave issues VALU work at about one instruction per 6 cycles, while a SIMD completes
+// one every 2.5-4.5 cycles when two or more waves issue: splitting a tile's score work
+// (code conversions, tile-scale combination, softmax) over two waves per head block puts
+// two VALU streams beside the value wave's matrix stream on each SIMD.
 //
 // Per 32-token tile:
 //   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
 //     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 5-slot
-//     ring of 752-byte rows (the stride at which both operand read patterns below run at
-//     the LDS's measured best); tile i+3's loads go out at the top of iteration i, after
-//     the wait for tiles i and i+1 (the score waves read tile i+1's keys).  Page ids
-//     come the same way, 3 tiles ahead, into a small LDS ring (a scalar load would make
-//     every later LDS wait also wait for it);
-//   * scores: the FP8 codes enter a scaled fp8 MFMA 16x16x128 as they are; Q is resident as
-//     two e4m3 terms with power-of-two scales per head and tile (q = hi 2^e_hi + lo 2^e_lo,
-//     exact to 2^-21 of the tile's max), so each 128-dim tile is two MFMAs.  The rope dims
-//     use bf16 MFMA 16x16x32.  The token scales are applied in fp32 to the per-tile
-//     partials: S = sum_t scale_t (q_t . k_t) + q_rope . k_rope.  (The FlashMLA walk-through
-//     dequantises to bf16 and runs bf16 MMA with fp32 accumulation, section 计算环节一; here
-//     no operand of the score product is converted.)
+//     ring of 752-byte rows; each score wave loads 4 tokens; tile i+3's loads go out at the
+//     top of iteration i, after the wait for tiles i and i+1 (the score waves read tile
+//     i+1's keys).  Page ids come the same way, 3 tiles ahead, into a small LDS ring (a
+//     scalar load would make every later LDS wait also wait for it);
+//   * scores: per 128-dim scale tile u, four bf16 MFMAs 16x16x32 on the codes converted
+//     in registers; rope dims: two bf16 MFMAs; S = sum_u scale_t,u (q_u . code_t,u) +
+//     q_rope . k_rope in fp32;
 //   * an online softmax per head column (the previous tile's, in the MFMA slots of the next
-//     tile's scores); the score wave writes P^T times each 128-dim value tile's token scales
-//     (bf16, the B operands of the PV MFMAs) and the factor for O^T (1 unless the reference
-//     max moved);
+//     tile's scores); the score waves write P^T times each 128-dim value tile's token
+//     scales (bf16, the B operands of the PV MFMAs; each wave its half of the tokens) and
+//     the factor for O^T (1 unless the reference max moved);
 //   * O^T += V^T . P^T with bf16 MFMA 16x16x32, V^T read transposed from the FP8 codes
 //     (ds_read_b64_tr_b8) and converted in registers (exact).  O^T takes 128 registers (the
 //     register-budget problem the FlashMLA walk-through describes in section 计算环节二),
-//     ordinary VGPRs: one kernel has one split between VGPRs and accumulation registers,
-//     and the score wave's registers are VGPRs.
-// Operand layouts.  QK row block sb (0, 1) of the A operand holds, in MFMA row m = 4g + r,
-// token 8g + 4sb + r, so lane group g of the S^T result holds tokens 8g..8g+7: exactly the
-// k slots the same lanes of a value wave feed to the PV MFMA (B = P^T, k = 8g + j), and
-// the transposed read returns tokens 8g..8g+7 of one value dim per lane; the PV operands
-// pass through LDS lane for lane.  In the fp8 MFMA lane (col, g) holds dims 16g + 0..15
-// and 64 + 16g + 0..15 of the 128-dim tile.
-// One workgroup barrier per tile: it publishes the PV operands of tile i-1 and frees the
-// ring slot of tile i-2.  The running max is only moved when a tile's max exceeds it by
-// more than 2^8, so the rescale of O^T is rare; probabilities stay below 2^8 and the result
-// is the same up to rounding (the reference cancels in the final normalisation).
+//     ordinary VGPRs.
+// Operand layouts.  QK row block sb of the A operand holds, in MFMA row m = 4g + r, token
+// 8g + 4sb + r, so lane group g of the S^T result holds tokens 8g + 4sb + 0..3: the k slots
+// 4sb .. 4sb+3 of lane group g of the PV B operand (B = P^T, k = 8g + j), and the
+// transposed read returns tokens 8g..8g+7 of one value dim per lane; the PV operands pass
+// through LDS lane for lane, each score wave writing its 8 bytes of the 16.  In a QK MFMA,
+// lane (col, g) holds dims 16g + 0..7, 16g + 8..15, 64 + 16g + 0..7, 64 + 16g + 8..15 of
+// the 128-dim tile (one per k-step), the same for K and Q.
+// One workgroup barrier per tile: it publishes the PV operands and half-tile maxima, and
+// frees the ring slot of tile i-2.  The running max is only moved when a tile's max
+// exceeds it by more than 2^8, so the rescale of O^T is rare; probabilities stay below 2^8
+// and the result is the same up to rounding (the reference cancels in the final
+// normalisation).
 //
 // Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
 // indices): the items then cover index slots, and slot k of request b names the key
 // position indices[b][k].  The address of a listed token takes two dependent lookups
-// (index, then block table); lanes 0-3 of each wave (its 4 tokens of a tile) load them
-// direct to LDS, positions 6 tiles and page ids 3 tiles ahead of the tile's own loads,
-// so that every wait for them is one the KV ring does anyway.  A slot outside the item or
-// the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
+// (index, then block table); lanes 0-3 of each score wave (its 4 tokens of a tile) load
+// them direct to LDS, positions 6 tiles and page ids 3 tiles ahead of the tile's own
+// loads, so that every wait for them is one the KV ring does anyway.  A slot outside the
+// item or the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
 // applied in the softmax.
 #include "pa_internal.h"
 #include "pa_merge.h"
@@ -84,18 +87,24 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+struct u32x4x2 {
+    u32x4 x, y;
+};
 
 #define PA_LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 8;                          // 4 score waves, then 4 value waves
+constexpr int kScoreWaves = 8;                     // head block hg = w & 3, row block sb = w >> 2
+constexpr int kValueWaves = 4;                     // value tile vt = w & 3
+constexpr int kWaves = kScoreWaves + kValueWaves;  // three per SIMD: waves w, w + 4, w + 8
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerWG = kWaves / 2 * kHeadsPerWave;   // 64
+constexpr int kHeadsPerWG = 4 * kHeadsPerWave;     // 64
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kTokBytes = 656;
 constexpr int kChunks = kTokBytes / 16;            // 41 16-byte chunks per token
 constexpr int kT = 32;                             // tokens per tile
-constexpr int kTokPerWave = kT / kWaves;           // 4 tokens loaded per wave and tile
+constexpr int kLoadWaves = kValueWaves;           // the value waves issue the tile loads
+constexpr int kTokPerWave = kT / kLoadWaves;       // 8 tokens loaded per value wave and tile
 constexpr int kRawRow = 752;                       // LDS row of a token (656 + 96)
 constexpr int kRawTile = kT * kRawRow;             // 24064
 constexpr int kRawSlots = 5;                       // tile ring
@@ -108,6 +117,7 @@ constexpr int kVBlocks = 128 / 16;                 // 16-dim blocks of a value w
 constexpr float kLazyMax = 8.0f;                   // log2 units
 
 static_assert(kRawSlots >= 4, "the tile loop reads tiles i and i-1 with loads in flight");
+static_assert(kTokPerWave == 128 / 16, "a value wave issues one token load per 16-dim block of its PV");
 static_assert(kLookRing > 2 * kAhead && (kLookRing & (kLookRing - 1)) == 0, "lookup ring");
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -115,7 +125,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 template <bool SPARSE>
 struct MlaCfg {
-    // loads per wave and tile: one per token, one page-id load (sparse: plus one index load)
+    // loads per value wave and tile: one per token, one page-id load (sparse: plus one index
+    // load)
     static constexpr int kLoadsPerTile = SPARSE ? kTokPerWave + 2 : kTokPerWave + 1;
 };
 
@@ -189,60 +200,6 @@ __device__ __forceinline__ float col_sum(float x)
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Q as two fp8 terms for the scaled fp8 MFMA: hi = e4m3(v 2^-e_hi), lo = e4m3((v - hi
-// 2^e_hi) 2^-e_lo), with e the power of two that brings the max |.| over the head's 128
-// dims (this lane's 32 and those of lanes l^16, l^32, l^48) into [128, 256), within the
-// E8M0 range.  A bf16 value has 8 significant bits and each term keeps 4, so hi + lo is v
-// exactly for every v within 2^13 of the maximum, and within 2^-21 of it otherwise.
-__device__ __forceinline__ int split_exp(float mx)
-{
-    return max(__builtin_amdgcn_frexp_expf(col_max(mx)) - 8, -127);
-}
-__device__ __forceinline__ int fp8x4_code(const float *v, int e)
-{
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[0], -e), __builtin_amdgcn_ldexpf(v[1], -e), 0, false);
-    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[2], -e), __builtin_amdgcn_ldexpf(v[3], -e), w, true);
-}
-__device__ __forceinline__ int q_split_exp(const float (&v)[32])
-{
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(v[i]));
-    return split_exp(mx);
-}
-__device__ __forceinline__ int q_split_lo(const float (&v)[32], int e_hi, i32x8 &hi, i32x8 &lo)
-{
-    float r[32], mx = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-        const int w = fp8x4_code(&v[4 * d], e_hi);
-        hi[d] = w;
-        const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        r[4 * d + 0] = v[4 * d + 0] - __builtin_amdgcn_ldexpf(x0[0], e_hi);
-        r[4 * d + 1] = v[4 * d + 1] - __builtin_amdgcn_ldexpf(x0[1], e_hi);
-        r[4 * d + 2] = v[4 * d + 2] - __builtin_amdgcn_ldexpf(x1[0], e_hi);
-        r[4 * d + 3] = v[4 * d + 3] - __builtin_amdgcn_ldexpf(x1[1], e_hi);
-    }
-#pragma unroll
-    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(r[i]));
-    const int e_lo = split_exp(mx);
-#pragma unroll
-    for (int d = 0; d < 8; d++) lo[d] = fp8x4_code(&r[4 * d], e_lo);
-    return e_lo;
-}
-
-// scaled fp8 MFMA 16x16x128 (both operands e4m3): A unscaled, B scaled by byte u of sc
-__device__ __forceinline__ f32x4 mfma_fp8_q(int u, const i32x8 &a, const i32x8 &b, const f32x4 &c, uint32_t sc)
-{
-    switch (u) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, (int)sc);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 1, (int)sc);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 2, (int)sc);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 3, (int)sc);
-    }
-}
-
 // O^T += A B in place, as inline asm: the accumulator is tied to its registers (with the
 // builtin the compiler may rename O^T's blocks from one tile to the next and copy them
 // back at the loop edge, 4 cycles per register), and they are ordinary VGPRs: one
@@ -273,28 +230,31 @@ __device__ __forceinline__ void mfma_acc_drain(f32x4 (&acc)[N])
 // (draft tokens' causal limits, a sliding window); separate instantiations keep the plain
 // kernel's registers free.
 template <bool SPARSE, bool MASKED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pa_mla_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void pa_mla_kernel(
     DecodeArgs a, const int32_t *__restrict__ plan, const int32_t *__restrict__ bt, int ngroups,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ indices)
 {
     constexpr int kLoadsPerTile = MlaCfg<SPARSE>::kLoadsPerTile;
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
-    // the PV B operands of a tile from the score wave of head block hg, in its lanes' layout
-    // (lane (col, g4): head col, tokens 8g4 + 0..7): P^T times value tile t's token scales,
-    // bf16: [tile parity][hg][value tile t][lane]
+    // the PV B operands of a tile from the score waves of head block hg, in their lanes'
+    // layout (lane (col, g4): head col, tokens 8g4 + 0..7, row block sb's 4 in bytes 8sb ..
+    // 8sb+7): P^T times value tile t's token scales, bf16: [tile parity][hg][value tile t][lane]
     __shared__ bf16x8 s_p[2][4][4][64];
     __shared__ float s_alpha[2][4][16];       // factor on O^T before the tile's PV, per head
+    __shared__ float s_tmax[2][2][4][16];     // [tile parity][sb][hg][head]: half-tile maxima
+    __shared__ float s_lsum[2][4][16];        // [sb][hg][head]: the halves' row sums
     __shared__ float s_inv[4][16];            // the item's final 1 / l, per head
     __shared__ int s_flag;                    // fused combine: this workgroup merges
-    __shared__ __attribute__((aligned(4))) uint8_t s_valid[kRawSlots][kWaves];   // sparse: real-token bits
-    // lookups: [position | page id][tile % kLookRing][wave][token] (dense: page ids of the
-    // wave's first token only)
-    __shared__ int32_t s_look[2 * kLookRing * kWaves * kTokPerWave];
+    __shared__ __attribute__((aligned(4))) uint8_t s_valid[kRawSlots][kLoadWaves];   // sparse: real-token bits
+    // lookups: [position | page id][tile % kLookRing][load wave][token] (dense: page ids of
+    // the wave's first token only)
+    __shared__ int32_t s_look[2 * kLookRing * kLoadWaves * kTokPerWave];
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int hg = wave & 3;                       // score: head block; value: value tile (same SIMD)
-    const bool scorer = wave < 4;                  // score wave; else value wave
+    const bool scorer = wave < kScoreWaves;        // score wave; else value wave
+    const int sb = (wave >> 2) & 1;                // score wave: row block of each tile
     // workgroup id -> (part, head group): the head groups of one part are 8 ids apart
     const int wg = blockIdx.x;
     const int part = (wg / (8 * ngroups)) * 8 + wg % 8;
@@ -308,476 +268,536 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int col = lane & 15, g4 = lane >> 4;     // MFMA column (head), lane group
     const int page_mask = (1 << a.page_shift) - 1;
 
-    // LDS byte offsets inside a tile slot: the QK operand rows of row block 0 (token
-    // 8(col/4) + col%4 at this lane's 16 bytes of each 64-dim group; row block 1 is 4 rows
-    // further), the rope operand, the scale rows of this lane's tokens 8g4 + r, and the
-    // transposed PV read (lane pair 2r, 2r+1 of a 16-lane block supplies row 8g4 + r,
-    // bytes 0-7 and 8-15 of the block's 16 value dims)
-    const uint32_t qk_off = (uint32_t)((8 * (col >> 2) + (col & 3)) * kRawRow + 16 * g4);
+    // LDS byte offsets inside a tile slot: the QK operand rows of this wave's row block
+    // (token 8(col/4) + 4 sb + col%4 at this lane's 16 bytes of each 64-dim group), the
+    // rope operand, the scale rows of this lane's tokens 8g4 + 4sb + r, and the transposed
+    // PV read (lane pair 2r, 2r+1 of a 16-lane block supplies row 8g4 + r, bytes 0-7 and
+    // 8-15 of the block's 16 value dims)
+    const uint32_t qk_off = (uint32_t)((8 * (col >> 2) + 4 * sb + (col & 3)) * kRawRow + 16 * g4);
     const uint32_t rope_off = qk_off + 528;
-    const uint32_t sc_off = (uint32_t)(8 * g4 * kRawRow + 512);
+    const uint32_t sc_off = (uint32_t)((8 * g4 + 4 * sb) * kRawRow + 512);
     const uint32_t pv_off = (uint32_t)((8 * g4 + ((lane & 15) >> 1)) * kRawRow + 8 * (lane & 1));
 
     // a fixed-split plan has exactly one item per part (no plan read on the critical path)
     const int ib = a.fixed_splits > 0 ? part : plan[a.part_begin_off + part];
     const int ie = a.fixed_splits > 0 ? part + 1 : plan[a.part_begin_off + part + 1];
 
-    for (int it = ib; it < ie; it++) {
-        const int b = plan[a.items_off + 4 * it + 0];
-        const int t0 = plan[a.items_off + 4 * it + 1];
-        const int t1 = plan[a.items_off + 4 * it + 2];
-        const int flags = plan[a.items_off + 4 * it + 3];
-        const int ntiles = (t1 - t0 + kT - 1) / kT;
-        const int64_t qr = (int64_t)qi * Hq + head0 + col;     // query row within the request
+    // The two roles run the same items with the same barrier sequence, each in its own
+    // loop (values one role keeps across its items then never occupy the other's registers).
+    if (scorer) {
+        for (int it = ib; it < ie; it++) {
+            const int b = plan[a.items_off + 4 * it + 0];
+            const int t0 = plan[a.items_off + 4 * it + 1];
+            const int t1 = plan[a.items_off + 4 * it + 2];
+            const int flags = plan[a.items_off + 4 * it + 3];
+            const int ntiles = (t1 - t0 + kT - 1) / kT;
+            const int64_t qr = (int64_t)qi * Hq + head0 + col;     // query row within the request
 
-        // ---- lookups.  Sparse: lane l < 4 loads those of token l of the wave's 4 in tile j,
-        //      index slot k.  Dense: lane 0 loads the page id of the wave's first token of
-        //      tile j (its 4 tokens are consecutive slots of one page).
-        const int Lb = SPARSE ? seq_lens[b] : 0;
-        auto sp_slot = [&](int j) { return t0 + kT * j + kTokPerWave * wave + (lane & (kTokPerWave - 1)); };
-        auto look = [&](int which, int j) {
-            return &s_look[((which * kLookRing + (j & (kLookRing - 1))) * kWaves + wave) * kTokPerWave];
-        };
-        auto sp_issue_pos = [&](int j) {           // slots past the row: its last entry
-            if (lane < kTokPerWave)
-                lds_dma_glb4(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1), lds_addr(look(0, j)));
-        };
-        auto sp_issue_page = [&](int j, int pos) { // no real token: the row's first page
-            const bool ok = sp_slot(j) < t1 && pos >= 0 && pos < Lb;
-            if (lane < kTokPerWave)
-                lds_dma_glb4(bt + (int64_t)b * a.max_pages + (ok ? pos >> a.page_shift : 0), lds_addr(look(1, j)));
-        };
-        auto sp_read = [&](int which, int j) {     // a lookup that is in; lane l: token l % 4
-            int v;
-            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v)
-                         : "v"(lds_addr(look(which, j)) + 4 * (lane & (kTokPerWave - 1))) : "memory");
-            return v;
-        };
-        auto dn_issue_page = [&](int j) {          // past the item: its last token's page
-            if (lane == 0)
-                lds_dma_glb4(bt + (int64_t)b * a.max_pages + (min(t0 + kT * j + kTokPerWave * wave, t1 - 1) >> a.page_shift),
-                             lds_addr(look(1, j)));
-        };
-        // dense: the page id of tile t (uniform), read from LDS; the value exists only after
-        // its wait, inside the same asm statement (an intrinsic on the loaded register could
-        // be moved above a separate wait).  page_barrier also does the loop top's barrier,
-        // with the read in flight across it.
-        auto dn_page = [&](int t) {
-            int v, pg;
-            asm volatile("ds_read_b32 %0, %2\n\ts_waitcnt lgkmcnt(0)\n\tv_readfirstlane_b32 %1, %0"
-                         : "=&v"(v), "=s"(pg) : "v"(lds_addr(look(1, t))) : "memory");
-            return pg;
-        };
-        auto page_barrier = [&](int t) {
-            int v, pg;
-            asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b32 %0, %2\n\ts_barrier\n\ts_waitcnt lgkmcnt(0)\n\t"
-                         "v_readfirstlane_b32 %1, %0"
-                         : "=&v"(v), "=s"(pg) : "v"(lds_addr(look(1, t))) : "memory");
-            return pg;
-        };
+            // ---- the value waves load the tiles; top of tile i: all waves are past tile i-1
+            //      and tiles i and i + 1 are in LDS
+            auto tile_top = [&](int) { lds_barrier(); };
+            if (ntiles > 0) lds_barrier();                   // tile 0 is in
 
-        // ---- loads of tile t into its ring slot: token tt of the wave (tile row 4 wave + tt)
-        //      by lanes 0-40 through a buffer over that token's 656 bytes, or over none (reads
-        //      as zeros) when it is not real.  Sparse: the page ids of tile t + kAhead and the
-        //      positions of tile t + 2 kAhead go out first; the lookups this uses were loaded
-        //      kAhead tiles ago.  Dense: the page id of tile t + kAhead goes out last.
-        auto issue_tile = [&](int t, int page) {
-            uint8_t *dst = &raw[t % kRawSlots][kTokPerWave * wave * kRawRow];
-            if (SPARSE) {
-                const int pos_look = sp_read(0, t + kAhead);
-                sp_issue_page(t + kAhead, pos_look);
-                sp_issue_pos(t + 2 * kAhead);
-                const int pos = sp_read(0, t), pgv = sp_read(1, t);
-                uint32_t vm = 0;
-#pragma unroll
-                for (int tt = 0; tt < kTokPerWave; tt++) {
-                    const int p = __builtin_amdgcn_readlane(pos, tt);
-                    const int pg = __builtin_amdgcn_readlane(pgv, tt);
-                    const int k = t0 + kT * t + kTokPerWave * wave + tt;
-                    const bool ok = k < t1 && p >= 0 && p < Lb;
-                    vm |= (ok ? 1u : 0u) << tt;
-                    const uint8_t *src = a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0);
-                    if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, lds_addr(dst + tt * kRawRow));
+                // ================= score wave (hg, sb): S, softmax and P of row block sb of tile i
+                // causal limit of the block's draft token and the first key its window leaves
+                int tlim = t1, tlo = 0;
+                if (MASKED) {
+                    const int L = seq_lens[b];
+                    if (nq > 1) tlim = min(t1, L - (nq - 1 - qi));
+                    if (a.window > 0) tlo = max(0, L - nq + qi - a.window + 1);
                 }
-                if (lane == 0) s_valid[t % kRawSlots][wave] = (uint8_t)vm;
-            } else {
-                // the 4 tokens are consecutive slots of one page
-                const int tw = t0 + kT * t + kTokPerWave * wave;     // first of the 4 tokens
-                const uint8_t *tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
-                const int nreal = min(max(t1 - tw, 0), kTokPerWave);
-                const uint32_t lds0 = lds_addr(dst);
+                // Q^T of the block's 16 heads (B of the MFMAs), resident, bf16.  Latent tile u,
+                // k-step e: lane (col, g4) holds dims 128u + 64(e >> 1) + 16g4 + 8(e & 1) .. +7.
+                // Rope: step r <- dims 512 + 32r + 8g4 .. +7.  A block with no query rows runs on
+                // a zero Q and writes nothing.
+                bf16x8 qb[4][4], qrope[2];
+                {
+                    const uint16_t *qrow = a.q + ((int64_t)b * nq * Hq + qr) * kDqk;
 #pragma unroll
-                for (int tt = 0; tt < kTokPerWave; tt++)
-                    if (lane < kChunks)
-                        lds_dma_buf16(tok + (int64_t)tt * a.s_tok_b, tt < nreal ? kTokBytes : 0, 16 * lane, lds0 + tt * kRawRow);
-                dn_issue_page(t + kAhead);
-            }
-        };
-
-        // ---- top of tile i (both roles, same barriers): tile i's loads in (tiles i+1 ..
-        //      i+kAhead-1 are younger), all waves past tile i-1 (slot of tile i-2 free, the
-        //      B operands of tile i-1 stored), then tile i+kAhead's loads into its slot (every
-        //      wave issues exactly one tile's loads per iteration, which the wait counts rely
-        //      on; issued here or spread between the MFMAs measured the same)
-        auto tile_top = [&](int i) {
-            wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
-            if (SPARSE) {
-                lds_barrier();
-                issue_tile(i + kAhead, 0);
-            } else {
-                issue_tile(i + kAhead, page_barrier(i + kAhead));
-            }
-        };
-
-        if (ntiles > 0) {
-            // ---- prologue: lookups (sparse), the loads of tiles 0..kAhead-1
-            if (SPARSE) {
-                for (int t = 0; t < 2 * kAhead; t++) sp_issue_pos(t);
-                wait_vmcnt<0>();
-                for (int t = 0; t < kAhead; t++) sp_issue_page(t, sp_read(0, t));
-            } else {
-                for (int t = 0; t < kAhead; t++) dn_issue_page(t);
-            }
-            wait_vmcnt<0>();
+                    for (int u = 0; u < 4; u++) {
 #pragma unroll
-            for (int t = 0; t < kAhead; t++) issue_tile(t, SPARSE ? 0 : dn_page(t));
-        }
-
-        if (scorer) {
-            // ================= score wave: S, softmax and P of tile i in iteration i
-            // causal limit of the block's draft token and the first key its window leaves
-            int tlim = t1, tlo = 0;
-            if (MASKED) {
-                const int L = seq_lens[b];
-                if (nq > 1) tlim = min(t1, L - (nq - 1 - qi));
-                if (a.window > 0) tlo = max(0, L - nq + qi - a.window + 1);
-            }
-            // Q^T of the block's 16 heads (B of the MFMAs), resident.  Latent tile u: an fp8
-            // pair per head, lane (col, g4) holding dims 128u + 16g4 + 0..15 (bytes 0-15) and
-            // 128u + 64 + 16g4 + 0..15 (bytes 16-31), the k order of the fp8 MFMA.  Rope: bf16,
-            // step r <- dims 512 + 32r + 8g4 .. +7.  A block with no query rows runs on a zero
-            // Q and writes nothing.
-            i32x8 qhi[4], qlo[4];
-            uint32_t qsc_hi = 0, qsc_lo = 0;          // E8M0 byte u: tile u
-            bf16x8 qrope[2];
-            {
-                const uint16_t *qrow = a.q + ((int64_t)b * nq * Hq + qr) * kDqk;
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    float v[32];
-                    u32x4 raw4[4];
-#pragma unroll
-                    for (int h = 0; h < 4; h++)
-                        raw4[h] = active ? *(const u32x4 *)(qrow + 128 * u + 64 * (h >> 1) + 16 * g4 + 8 * (h & 1))
-                                         : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int x = 0; x < 16; x++) {
-                        const uint32_t w2 = raw4[x >> 2][x & 3];
-                        v[2 * x] = __uint_as_float(w2 << 16);
-                        v[2 * x + 1] = __uint_as_float(w2 & 0xFFFF0000u);
+                        for (int e = 0; e < 4; e++)
+                            qb[u][e] = active ? *(const bf16x8 *)(qrow + 128 * u + 64 * (e >> 1) + 16 * g4 + 8 * (e & 1))
+                                              : bf16x8{};
                     }
-                    const int e_hi = q_split_exp(v);
-                    const int e_lo = q_split_lo(v, e_hi, qhi[u], qlo[u]);
-                    qsc_hi |= (uint32_t)(127 + e_hi) << (8 * u);
-                    qsc_lo |= (uint32_t)(127 + e_lo) << (8 * u);
+#pragma unroll
+                    for (int r = 0; r < 2; r++)
+                        qrope[r] = active ? *(const bf16x8 *)(qrow + 512 + 32 * r + 8 * g4) : bf16x8{};
                 }
-#pragma unroll
-                for (int r = 0; r < 2; r++)
-                    qrope[r] = active ? *(const bf16x8 *)(qrow + 512 + 32 * r + 8 * g4) : bf16x8{};
-            }
-            float m = -INFINITY;     // reference max (log2 domain) of head `col`
-            float l = 0.f;
+                float m = -INFINITY;     // reference max (log2 domain) of head `col`, both halves
+                float l = 0.f;           // this lane's share of the row sum (its 4 tokens)
 
-            // ---- S^T of tile t (rows: this lane's tokens 8g4 + 4sb + r) into st[8]: one partial
-            //      per 128-dim scale tile u (two scaled fp8 MFMAs 16x16x128, Q's hi and lo
-            //      terms) and one for the rope dims (two bf16 MFMAs 16x16x32), combined with
-            //      the token scales in fp32 as each pair of tiles completes.  MFMA slot k of row
-            //      block sb: rope 0, 1, tiles (0,1) hi, (0,1) lo, (2,3) hi, (2,3) lo; every
-            //      operand is read two slots before its first use.  step(s) runs in slot
-            //      s = 10 sb + k, before its MFMA: the VALU work of the previous tile, issued
-            //      while the matrix core works (and, first, while the tile's first reads
-            //      are on their way).
-            auto qk_tile = [&](int t, float (&st)[8], auto &&step) {
-                PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t % kRawSlots];
-                auto rd_codes = [&](int sb, int u) {
-                    PA_LDS const uint8_t *p = slot + qk_off + 4 * sb * kRawRow + 128 * u;
-                    const u32x4 x = *(PA_LDS const u32x4 *)p;
-                    const u32x4 y = *(PA_LDS const u32x4 *)(p + 64);
-                    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-                };
-                auto rd_rope = [&](int sb, int r) { return *(PA_LDS const bf16x8 *)(slot + rope_off + 4 * sb * kRawRow + 64 * r); };
-                i32x8 kc[2][4];
-                bf16x8 kr[2][2];
-                f32x4 part[2][5];
-                f32x4 sc[8];                       // token 8g4 + r's four tile scales
-                kr[0][0] = rd_rope(0, 0);
-                kr[0][1] = rd_rope(0, 1);
-                // rows 2h, 2h+1 of row block sb, tiles 2v and 2v+1: the token scales times the
-                // tile partials, added to the rope partial (v = 0) or the sum so far (v = 1)
-                auto combine = [&](int sb, int v, int h) {
+                // ---- S^T of row block sb of tile t (rows: this lane's tokens 8g4 + 4sb + r) into
+                //      st[4]: per 128-dim scale tile u an fp32 partial of 4 bf16 MFMAs on the
+                //      converted codes, one partial for the rope dims (2 bf16 MFMAs), combined
+                //      with the token scales in fp32 as the tiles complete.  MFMA slot k: tile
+                //      k / 4, step k % 4 for k < 16, then rope 0, 1; the A operand of slot k + 1
+                //      is converted in slot k, codes are read about 6 slots before their use.
+                //      step(k) runs in slot k, before its MFMA: the VALU work of the previous
+                //      tile, issued while the matrix core works.
+                auto qk_tile = [&](int t, float (&st)[4], auto &&step) {
+                    PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t % kRawSlots];
+                    auto rd_codes = [&](int u) {
+                        PA_LDS const uint8_t *p = slot + qk_off + 128 * u;
+                        const u32x4 x = *(PA_LDS const u32x4 *)p;
+                        const u32x4 y = *(PA_LDS const u32x4 *)(p + 64);
+                        return u32x4x2{x, y};
+                    };
+                    auto cvt = [&](const u32x4x2 &c, int e) {
+                        const u32x4 &w = (e >> 1) ? c.y : c.x;
+                        return (e & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
+                    };
+                    u32x4x2 kc[2];                     // codes of tiles u (kc[u & 1])
+                    bf16x8 kr[2];
+                    f32x4 part[5];
+                    float scu[2][4];                   // scale of tile u of token 8g4 + 4sb + r
+                    float x[4];
 #pragma unroll
-                    for (int r = 2 * h; r < 2 * h + 2; r++) {
-                        float x = v == 0 ? part[sb][4][r] : st[4 * sb + r];
+                    for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    auto rd_scales = [&](int u) {
 #pragma unroll
-                        for (int u = 2 * v; u < 2 * v + 2; u++) x += sc[4 * sb + r][u] * part[sb][u][r];
-                        asm volatile("" : "+v"(x));    // computed in this slot
-                        st[4 * sb + r] = x;
-                    }
-                };
+                        for (int r = 0; r < 4; r++)
+                            scu[u & 1][r] = *(PA_LDS const float *)(slot + sc_off + r * kRawRow + 4 * u);
+                    };
+                    kc[0] = rd_codes(0);
+                    bf16x8 av[2];
+                    av[0] = cvt(kc[0], 0);
 #pragma unroll
-                for (int sb = 0; sb < 2; sb++) {
-#pragma unroll
-                    for (int p = 0; p < 5; p++) part[sb][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int k = 0; k < 10; k++) {
-                        // reads issued at this slot (the token scales early, for the combine)
-                        if (k == 0) kc[sb][0] = rd_codes(sb, 0);
-                        if (k == 1) kc[sb][1] = rd_codes(sb, 1);
-                        if (k >= 2 && k < 6)
-                            sc[4 * sb + k - 2] = *(PA_LDS const f32x4 *)(slot + sc_off + (4 * sb + k - 2) * kRawRow);
-                        if (k == 4) kc[sb][2] = rd_codes(sb, 2);
-                        if (k == 5) kc[sb][3] = rd_codes(sb, 3);
-                        if (sb == 0 && k == 8) kr[1][0] = rd_rope(1, 0);
-                        if (sb == 0 && k == 9) kr[1][1] = rd_rope(1, 1);
-                        step(10 * sb + k);
-                        if (k < 2) {
-                            part[sb][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sb][k], qrope[k], part[sb][4], 0, 0, 0);
-                        } else {
-                            const int u = 2 * ((k - 2) >> 2) + (k & 1);
-                            const bool lo = ((k - 2) & 2) != 0;
-                            part[sb][u] = mfma_fp8_q(u, kc[sb][u], lo ? qlo[u] : qhi[u], part[sb][u], lo ? qsc_lo : qsc_hi);
+                    for (int k = 0; k < 18; k++) {
+                        // reads issued at this slot: the next tile's codes 4 slots before their
+                        // first use, the scales of tile u after its MFMAs start, rope at slot 10
+                        if (k < 16 && (k & 3) == 0 && k + 4 < 16) kc[((k >> 2) + 1) & 1] = rd_codes((k >> 2) + 1);
+                        if (k < 16 && (k & 3) == 1) rd_scales(k >> 2);
+                        if (k == 10) {
+                            kr[0] = *(PA_LDS const bf16x8 *)(slot + rope_off);
+                            kr[1] = *(PA_LDS const bf16x8 *)(slot + rope_off + 64);
                         }
-                        // tiles 0, 1 two slots after their last MFMA; tiles 2, 3 of row block
-                        // 0 under row block 1's first MFMAs
-                        if (k == 7 || k == 8) combine(sb, 0, k - 7);
-                        if (sb == 1 && (k == 1 || k == 2)) combine(0, 1, k - 1);
+                        step(k);
+                        if (k < 16) {
+                            part[k >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k & 1], qb[k >> 2][k & 3], part[k >> 2], 0, 0, 0);
+                        } else {
+                            part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k - 16], qrope[k - 16], part[4], 0, 0, 0);
+                        }
+                        if (k + 1 < 16) av[(k + 1) & 1] = cvt(kc[((k + 1) >> 2) & 1], (k + 1) & 3);
+                        // the token scales times the tile partials, three slots after a tile's
+                        // last MFMA (tile 3's and the rope partial after the loop)
+                        if (k == 6 || k == 10 || k == 14) {
+                            const int u = (k - 6) >> 2;
+#pragma unroll
+                            for (int r = 0; r < 4; r++) {
+                                float y = u == 0 ? 0.f : x[r];
+                                y += scu[u & 1][r] * part[u][r];
+                                asm volatile("" : "+v"(y));    // computed in this slot
+                                x[r] = y;
+                            }
+                        }
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                }
-                combine(1, 1, 0);
-                combine(1, 1, 1);
-            };
-
-            float st_cur[8];                   // S^T of the tile whose softmax is next
-            for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
-                tile_top(i);                   // tiles i and i + 1 are in LDS
-                if (i == ntiles) {
-                    break;
-                }
-                if (i == 0) qk_tile(0, st_cur, [](int) {});
-                // ---- softmax of tile i, spread over the MFMA slots of tile i + 1's S^T: logits
-                //      and mask, the max over the head's 32 tokens, the lazily moved reference,
-                //      p = 2^(s - m) and the row sum; P and the factor for O^T (1 unless the
-                //      reference moved) go to the value wave.  (Past the last tile, tile i + 1's
-                //      slot holds zeros and its result is unused.)
-                uint32_t vmask = 0;
-                if (SPARSE) {                      // tokens 8g4 .. 8g4+7: waves 2g4, 2g4+1
-                    const uint32_t v2 = *(const uint16_t *)&s_valid[i % kRawSlots][2 * g4];
-                    vmask = (v2 & 0xFu) | ((v2 >> 4) & 0xF0u);
-                }
-                float sv[8], bm = -INFINITY, m_new = m, alpha = 1.f, mref = 0.f, ps = 0.f;
-                float pr[8];
-                f32x4 scr[8];                      // tile i's token scales, read again
-                bf16x8 pb[4];
-                auto logits = [&](int r0) {
 #pragma unroll
-                    for (int r = r0; r < r0 + 4; r++) {
-                        const int tok = t0 + kT * i + 8 * g4 + r;
+                    for (int r = 0; r < 4; r++) st[r] = x[r] + scu[1][r] * part[3][r] + part[4][r];
+                };
+
+                // ---- logits of row block sb of tile t (log2 domain, masked) and their max per
+                //      head, published for the other half of the tile
+                float sv[4], bm_own = -INFINITY;
+                auto finish_tile = [&](int t, const float (&st)[4]) {
+                    uint32_t vmask = 0;
+                    if (SPARSE)                        // tokens 8g4 + 4sb + r: loader g4, bits 4sb + r
+                        vmask = (uint32_t)s_valid[t % kRawSlots][g4] >> (4 * sb);
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int tok = t0 + kT * t + 8 * g4 + 4 * sb + r;
                         const bool vis = SPARSE ? ((vmask >> r) & 1u) != 0
                                                 : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
-                        sv[r] = vis ? st_cur[r] * a.scale_log2 : -INFINITY;
-                        bm = fmaxf(bm, sv[r]);
+                        sv[r] = vis ? st[r] * a.scale_log2 : -INFINITY;
+                        mx = fmaxf(mx, sv[r]);
                     }
+                    bm_own = col_max(mx);
+                    if (g4 == 0) s_tmax[t & 1][sb][hg][col] = bm_own;
                 };
-                auto softmax_step = [&](int s) {
-                    if (s == 0) logits(0);
-                    if (s == 1) logits(4);
-                    if (s == 2) {
-                        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-                        bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+
+                {
+                    float st0[4];
+                    if (ntiles > 0) {
+                        qk_tile(0, st0, [](int) {});
+                        finish_tile(0, st0);
                     }
-                    if (s == 3) {
-                        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-                        bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
-                        m_new = bm > m + kLazyMax ? bm : m;
-                        alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
-                        mref = m_new == -INFINITY ? 0.f : m_new;
-                    }
-                    if (s >= 4 && s < 8) {
+                }
+                for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
+                    tile_top(i);                   // tiles i and i + 1 are in LDS, tile i's maxima out
+                    if (i == ntiles) break;
+                    // ---- softmax of tile i, spread over the MFMA slots of tile i + 1's S^T: the
+                    //      tile's max (both halves), the lazily moved reference, p = 2^(s - m) and
+                    //      this lane's row sum; P and the factor for O^T (1 unless the reference
+                    //      moved) go to the value wave.  (Past the last tile, tile i + 1's slot
+                    //      holds zeros and its result is unused.)
+                    float bm_other = 0.f, m_new = m, alpha = 1.f, mref = 0.f, ps = 0.f;
+                    float pr[4];
+                    f32x4 scr[2];                      // tile i's token scales, read again
+                    bf16x4 pb[4];
+                    auto softmax_step = [&](int s) {
+                        if (s == 0) bm_other = s_tmax[i & 1][sb ^ 1][hg][col];
+                        if (s == 2) {
+                            const float bm = fmaxf(bm_own, bm_other);
+                            m_new = bm > m + kLazyMax ? bm : m;
+                            alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
+                            mref = m_new == -INFINITY ? 0.f : m_new;
+                        }
+                        if (s == 3 || s == 4) {
 #pragma unroll
-                        for (int r = 2 * (s - 4); r < 2 * (s - 4) + 2; r++) {
-                            pr[r] = fast_exp2(sv[r] - mref);
-                            ps += pr[r];
+                            for (int r = 2 * (s - 3); r < 2 * (s - 3) + 2; r++) {
+                                pr[r] = fast_exp2(sv[r] - mref);
+                                ps += pr[r];
+                            }
+                        }
+                        if (s == 5) {
+                            l = l * alpha + ps;
+                            m = m_new;
+                        }
+                        // the value waves' B operands: P^T times each value tile's token scales
+                        // (the value is the key's first 512 dims, so the scales are the key tile
+                        // scales), from the scale rows read again one step before their use (row
+                        // q read in step 5 + q into scr[q & 1], used in step 6 + q)
+                        if (s >= 5 && s < 9)
+                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + (s - 5) * kRawRow);
+                        if (s >= 6 && s < 10) {
+                            const int r = s - 6;
+#pragma unroll
+                            for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * scr[r & 1][t]);
+                        }
+                        if (s == 11 || s == 12) {
+#pragma unroll
+                            for (int t = 2 * (s - 11); t < 2 * (s - 11) + 2; t++)
+                                *(bf16x4 *)((uint8_t *)&s_p[i & 1][hg][t][lane] + 8 * sb) = pb[t];
+                        }
+                        if (s == 13) {
+                            // both halves hold the same factor and both write it (no branch in the
+                            // body, which would let the compiler sink the MFMAs past it)
+                            s_alpha[i & 1][hg][col] = alpha;
+                        }
+                    };
+                    float st_nxt[4];
+                    qk_tile(i + 1, st_nxt, softmax_step);
+                    finish_tile(i + 1, st_nxt);
+                }
+
+                // ---- epilogue: the row sum of both halves, 1 / l (with a sink of a whole-request
+                //      item) and lse
+                l = col_sum(l);
+                if (g4 == 0) s_lsum[sb][hg][col] = l;
+                lds_barrier();                                   // both halves' sums out
+                if (sb == 0) {
+                    l = s_lsum[0][hg][col] + s_lsum[1][hg][col];
+                    float inv, lse_v;
+                    const float sk = (a.sinks && (flags & 1)) ? a.sinks[head0 + col] * 1.4426950408889634f : -INFINITY;
+                    const float M2 = fmaxf(m, sk);
+                    if (M2 == -INFINITY || (sk == -INFINITY && l == 0.f)) {
+                        inv = 0.f;                               // nothing to attend to
+                        lse_v = -INFINITY;
+                    } else {
+                        // a sink (whole-request items only; split requests get it in the merge)
+                        // joins the denominator: den = l 2^(m - M2) + 2^(sk - M2)
+                        const float fm = fast_exp2(m - M2);      // m = -inf: 0
+                        const float den = l * fm + fast_exp2(sk - M2);
+                        inv = fm / den;
+                        lse_v = (M2 + log2f(den)) * 0.69314718055994530942f;
+                    }
+                    if (g4 == 0) {
+                        s_inv[hg][col] = inv;
+                        if (active) {
+                            if (flags & 1) a.lse[(int64_t)b * nq * Hq + qr] = lse_v;
+                            else if (!SPARSE && a.counters) store_shared(a.ws_lse + (int64_t)it * nq * Hq + qr, lse_v);
+                            else a.ws_lse[(int64_t)it * nq * Hq + qr] = lse_v;
                         }
                     }
-                    if (s == 8) {
-                        l = l * alpha + ps;
-                        m = m_new;
-                    }
-                    // the value waves' B operands: P^T times each value tile's token scales
-                    // (the value is the key's first 512 dims, so the scales are the key tile
-                    // scales), two rows per slot, from scales read again four slots before
-                    if (s >= 5 && s < 9) {
-#pragma unroll
-                        for (int r = 2 * (s - 5); r < 2 * (s - 5) + 2; r++)
-                            scr[r] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + r * kRawRow);
-                    }
-                    if (s >= 9 && s < 13) {
-#pragma unroll
-                        for (int r = 2 * (s - 9); r < 2 * (s - 9) + 2; r++) {
-#pragma unroll
-                            for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * scr[r][t]);
-                        }
-                    }
-                    if (s == 13) {
-                        s_p[i & 1][hg][0][lane] = pb[0];
-                        s_p[i & 1][hg][1][lane] = pb[1];
-                    }
-                    if (s == 14) {
-                        s_p[i & 1][hg][2][lane] = pb[2];
-                        s_p[i & 1][hg][3][lane] = pb[3];
-                        // (the column's 4 lanes hold the same factor: no branch in the body, which
-                        // would let the compiler sink the MFMAs and their combines past it)
-                        s_alpha[i & 1][hg][col] = alpha;
-                    }
-                };
-                float st_nxt[8];
-                qk_tile(i + 1, st_nxt, softmax_step);
-#pragma unroll
-                for (int r = 0; r < 8; r++) st_cur[r] = st_nxt[r];
-            }
+                }
+                lds_barrier();                                   // s_inv out
+            wait_vmcnt<0>();
+            lds_barrier();                                   // the item's LDS is free
+        }
+    } else {
+        for (int it = ib; it < ie; it++) {
+            const int b = plan[a.items_off + 4 * it + 0];
+            const int t0 = plan[a.items_off + 4 * it + 1];
+            const int t1 = plan[a.items_off + 4 * it + 2];
+            const int flags = plan[a.items_off + 4 * it + 3];
+            const int ntiles = (t1 - t0 + kT - 1) / kT;
+            const int64_t qr = (int64_t)qi * Hq + head0 + col;     // query row within the request
 
-            // ---- epilogue: 1 / l (with a sink of a whole-request item) and lse
-            l = col_sum(l);
-            float inv, lse_v;
-            const float sk = (a.sinks && (flags & 1)) ? a.sinks[head0 + col] * 1.4426950408889634f : -INFINITY;
-            const float M2 = fmaxf(m, sk);
-            if (M2 == -INFINITY || (sk == -INFINITY && l == 0.f)) {
-                inv = 0.f;                                   // nothing to attend to
-                lse_v = -INFINITY;
-            } else {
-                // a sink (whole-request items only; split requests get it in the merge)
-                // joins the denominator: den = l 2^(m - M2) + 2^(sk - M2)
-                const float fm = fast_exp2(m - M2);          // m = -inf: 0
-                const float den = l * fm + fast_exp2(sk - M2);
-                inv = fm / den;
-                lse_v = (M2 + log2f(den)) * 0.69314718055994530942f;
-            }
-            if (g4 == 0) {
-                s_inv[hg][col] = inv;
-                if (active) {
-                    if (flags & 1) a.lse[(int64_t)b * nq * Hq + qr] = lse_v;
-                    else if (!SPARSE && a.counters) store_shared(a.ws_lse + (int64_t)it * nq * Hq + qr, lse_v);
-                    else a.ws_lse[(int64_t)it * nq * Hq + qr] = lse_v;
-                }
-            }
-            lds_barrier();                                   // s_inv out
-        } else {
-            // ================= value wave: O^T += V^T P^T of tile i-1 in iteration i, for
-            // value tile vt = hg (dims 128 vt .. +127) and all 4 head blocks: O^T block
-            // acc[4 d + hb] holds dims 128 vt + 16 d + (4 g4 + e) of head col of block hb, so
-            // each V^T operand is read and converted once and feeds 4 MFMAs
-            const int vt = hg;
-            f32x4 acc[kDvBlocks];
-#pragma unroll
-            for (int d = 0; d < kDvBlocks; d++) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int lw = wave - kScoreWaves;               // loader index
+            // ---- lookups.  Sparse: lane l < 8 loads those of token l of the wave's 8 in tile
+            //      j, index slot k.  Dense: lane 0 loads the page id of the wave's first token of
+            //      tile j (its 8 tokens are consecutive slots of one page: tiles start at
+            //      multiples of 32 tokens and pages hold a multiple of 16).
+            const int Lb = SPARSE ? seq_lens[b] : 0;
+            auto sp_slot = [&](int j) { return t0 + kT * j + kTokPerWave * lw + (lane & (kTokPerWave - 1)); };
+            auto look = [&](int which, int j) {
+                return &s_look[((which * kLookRing + (j & (kLookRing - 1))) * kLoadWaves + lw) * kTokPerWave];
+            };
+            auto sp_issue_pos = [&](int j) {           // slots past the row: its last entry
+                if (lane < kTokPerWave)
+                    lds_dma_glb4(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1), lds_addr(look(0, j)));
+            };
+            auto sp_issue_page = [&](int j, int pos) { // no real token: the row's first page
+                const bool ok = sp_slot(j) < t1 && pos >= 0 && pos < Lb;
+                if (lane < kTokPerWave)
+                    lds_dma_glb4(bt + (int64_t)b * a.max_pages + (ok ? pos >> a.page_shift : 0), lds_addr(look(1, j)));
+            };
+            auto sp_read = [&](int which, int j) {     // a lookup that is in; lane l: token l % 4
+                int v;
+                asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v)
+                             : "v"(lds_addr(look(which, j)) + 4 * (lane & (kTokPerWave - 1))) : "memory");
+                return v;
+            };
+            auto dn_issue_page = [&](int j) {          // past the item: its last token's page
+                if (lane == 0)
+                    lds_dma_glb4(bt + (int64_t)b * a.max_pages + (min(t0 + kT * j + kTokPerWave * lw, t1 - 1) >> a.page_shift),
+                                 lds_addr(look(1, j)));
+            };
+            // dense: the page id of tile t (uniform), read from LDS; the value exists only after
+            // its wait, inside the same asm statement (an intrinsic on the loaded register could
+            // be moved above a separate wait).  page_barrier also does the loop top's barrier,
+            // with the read in flight across it.
+            auto dn_page = [&](int t) {
+                int v, pg;
+                asm volatile("ds_read_b32 %0, %2\n\ts_waitcnt lgkmcnt(0)\n\tv_readfirstlane_b32 %1, %0"
+                             : "=&v"(v), "=s"(pg) : "v"(lds_addr(look(1, t))) : "memory");
+                return pg;
+            };
+            auto page_barrier = [&](int t) {
+                int v, pg;
+                asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b32 %0, %2\n\ts_barrier\n\ts_waitcnt lgkmcnt(0)\n\t"
+                             "v_readfirstlane_b32 %1, %0"
+                             : "=&v"(v), "=s"(pg) : "v"(lds_addr(look(1, t))) : "memory");
+                return pg;
+            };
 
-            // V^T reads: tile j's dims 128 vt + 16 d + col, tokens 8g4 + 0..7 (lane); the 8
-            // reads of the next tile go out before the barrier (the tile is in LDS since the
-            // top of this iteration)
-            // (the base is made opaque, so that the reads become base + immediate offset and
-            // the compiler does not hoist a register per read)
-            auto vbase = [&](int t) {
-                uint32_t x = lds_addr(raw[t % kRawSlots]) + pv_off + 128 * vt;
-                asm volatile("" : "+v"(x));
-                return (PA_LDS uint8_t *)(uintptr_t)x;
+            // ---- loads of tile t into its ring slot: token tt of value wave lw (tile row
+            //      8 lw + tt) by lanes 0-40 through a buffer over that token's 656 bytes,
+            //      or over none (reads as zeros) when it is not real.  prep_tile works out
+            //      where the tokens are (sparse: the page ids of tile t + kAhead and the
+            //      positions of tile t + 2 kAhead go out first; the lookups this uses were
+            //      loaded kAhead tiles ago), dma_token issues one token's load, end_tile the
+            //      tile's last load (dense: the page id of tile t + kAhead).  The value waves
+            //      issue a tile's 8 token loads one per 16-dim block of their PV MFMAs: a
+            //      burst of all of them at the loop top stalls the issue for hundreds of cycles.
+            struct TileLoads {
+                const uint8_t *tok;                // dense: the first token's bytes
+                int nreal;                         // dense: real tokens of the 8
+                int pos, pgv;                      // sparse: lane l: token l's position, page id
+                uint32_t lds0;                     // LDS row of the first token
             };
-            auto rd = [&](PA_LDS uint8_t *vb, int d) {
-                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2 *)(vb + 16 * d));
-            };
-            i32x2 vw[kVBlocks];
-            for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
-                tile_top(i);
-                if (i > 0) {
-                    const int j = i - 1;
-                    // the tile's factors for O^T and the B operands (P^T of head block hb
-                    // times value tile vt's token scales, from the score wave of hb)
-                    float alpha[4];
-                    bf16x8 pbt[4];
+            auto prep_tile = [&](int t, int page) {
+                TileLoads L;
+                L.lds0 = lds_addr(&raw[t % kRawSlots][kTokPerWave * lw * kRawRow]);
+                L.tok = nullptr;
+                L.nreal = 0;
+                L.pos = L.pgv = 0;
+                if (SPARSE) {
+                    const int pos_look = sp_read(0, t + kAhead);
+                    sp_issue_page(t + kAhead, pos_look);
+                    sp_issue_pos(t + 2 * kAhead);
+                    L.pos = sp_read(0, t);
+                    L.pgv = sp_read(1, t);
+                    uint32_t vm = 0;
 #pragma unroll
-                    for (int hb = 0; hb < 4; hb++) {
-                        alpha[hb] = s_alpha[j & 1][hb][col];
-                        pbt[hb] = s_p[j & 1][hb][vt][lane];
+                    for (int tt = 0; tt < kTokPerWave; tt++) {
+                        const int p = __builtin_amdgcn_readlane(L.pos, tt);
+                        const int k = t0 + kT * t + kTokPerWave * lw + tt;
+                        vm |= (k < t1 && p >= 0 && p < Lb ? 1u : 0u) << tt;
                     }
-                    if (__any(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
-                        mfma_acc_drain(acc);                 // rare: a reference moved
-#pragma unroll
-                        for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha[d & 3];
-                        mfma_acc_drain(acc);                 // (wait states before the MFMAs)
-                    }
-                    // A = V^T converted to bf16 two blocks ahead; the first two get their wait
-                    // states before the first MFMA explicitly (the asm MFMAs are invisible to
-                    // the compiler's hazard checks)
-                    bf16x8 va[3];
-                    va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
-                    va[1] = fp8x8_to_bf16((uint32_t)vw[1][0], (uint32_t)vw[1][1]);
-                    asm volatile("s_nop 1" : "+v"(va[0]), "+v"(va[1]));
-#pragma unroll
-                    for (int d = 0; d < kVBlocks; d++) {
-#pragma unroll
-                        for (int hb = 0; hb < 4; hb++) mfma_acc(acc[4 * d + hb], va[d % 3], pbt[hb]);
-                        if (d + 2 < kVBlocks)
-                            va[(d + 2) % 3] = fp8x8_to_bf16((uint32_t)vw[d + 2][0], (uint32_t)vw[d + 2][1]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                if (i < ntiles) {
-                    PA_LDS uint8_t *vbn = vbase(i);
-#pragma unroll
-                    for (int d = 0; d < kVBlocks; d++) vw[d] = rd(vbn, d);
-                }
-            }
-            mfma_acc_drain(acc);
-            lds_barrier();                                   // s_inv in
-            // ---- epilogue: rows of head block hb: draft token and heads as in the score wave
-#pragma unroll
-            for (int hb = 0; hb < 4; hb++) {
-                const int r0 = group * kHeadsPerWG + hb * kHeadsPerWave;
-                if (r0 >= G * nq) continue;                  // no query rows
-                const int q_i = r0 / G;
-                const int64_t row = (int64_t)q_i * Hq + (r0 - q_i * G) + col;
-                const float inv = s_inv[hb][col];
-                if (flags & 1) {
-                    uint16_t *orow = a.out + ((int64_t)b * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
-#pragma unroll
-                    for (int d = 0; d < kVBlocks; d++) {
-                        bf16x4 o;
-#pragma unroll
-                        for (int e = 0; e < 4; e++) o[e] = (__bf16)(acc[4 * d + hb][e] * inv);
-                        *(bf16x4 *)(orow + 16 * d) = o;
-                    }
+                    L.nreal = (int)vm;             // sparse: the real-token bits
+                    if (lane == 0) s_valid[t % kRawSlots][lw] = (uint8_t)vm;
                 } else {
-                    float *orow = a.ws_o + ((int64_t)it * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
-                    if (!SPARSE && a.counters) {         // merged inside this launch
+                    // the 8 tokens are consecutive slots of one page
+                    const int tw = t0 + kT * t + kTokPerWave * lw;     // first of the 8 tokens
+                    L.tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
+                    L.nreal = min(max(t1 - tw, 0), kTokPerWave);
+                }
+                return L;
+            };
+            auto dma_token = [&](const TileLoads &L, int tt) {
+                if (SPARSE) {
+                    const int p = __builtin_amdgcn_readlane(L.pos, tt);
+                    const int pg = __builtin_amdgcn_readlane(L.pgv, tt);
+                    const bool ok = (L.nreal >> tt) & 1;
+                    const uint8_t *src = a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0);
+                    if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tt * kRawRow);
+                } else {
+                    if (lane < kChunks)
+                        lds_dma_buf16(L.tok + (int64_t)tt * a.s_tok_b, tt < L.nreal ? kTokBytes : 0, 16 * lane,
+                                      L.lds0 + tt * kRawRow);
+                }
+            };
+            auto end_tile = [&](int t) {
+                if (!SPARSE) dn_issue_page(t + kAhead);
+            };
+            auto issue_tile = [&](int t, int page) {
+                const TileLoads L = prep_tile(t, page);
+#pragma unroll
+                for (int tt = 0; tt < kTokPerWave; tt++) dma_token(L, tt);
+                end_tile(t);
+            };
+
+            // ---- top of tile i (all waves, same barriers): each value wave waits for its
+            //      loads of tile i+1 (tiles up to i+kAhead-1 are in flight, the younger one may
+            //      stay), all waves are past tile i-1 (slot of tile i-2 free, the B operands and
+            //      half maxima of tile i-1's iteration stored); returns where the loads of tile
+            //      i+kAhead go (each value wave issues exactly one tile's loads per iteration,
+            //      which the wait counts rely on)
+            auto tile_top = [&](int i) {
+                wait_vmcnt<(kAhead - 2) * kLoadsPerTile>();
+                if (SPARSE) {
+                    lds_barrier();
+                    return prep_tile(i + kAhead, 0);
+                } else {
+                    return prep_tile(i + kAhead, page_barrier(i + kAhead));
+                }
+            };
+
+            if (ntiles > 0) {
+                // ---- prologue: lookups (sparse), the loads of tiles 0..kAhead-1; tile 0 in
+                {
+                    if (SPARSE) {
+                        for (int t = 0; t < 2 * kAhead; t++) sp_issue_pos(t);
+                        wait_vmcnt<0>();
+                        for (int t = 0; t < kAhead; t++) sp_issue_page(t, sp_read(0, t));
+                    } else {
+                        for (int t = 0; t < kAhead; t++) dn_issue_page(t);
+                    }
+                    wait_vmcnt<0>();
+#pragma unroll
+                    for (int t = 0; t < kAhead; t++) issue_tile(t, SPARSE ? 0 : dn_page(t));
+                    wait_vmcnt<(kAhead - 1) * kLoadsPerTile>();
+                }
+                lds_barrier();
+            }
+
+                // ================= value wave: O^T += V^T P^T of tile i-1 in iteration i, for
+                // value tile vt = hg (dims 128 vt .. +127) and all 4 head blocks: O^T block
+                // acc[4 d + hb] holds dims 128 vt + 16 d + (4 g4 + e) of head col of block hb, so
+                // each V^T operand is read and converted once and feeds 4 MFMAs
+                const int vt = hg;
+                f32x4 acc[kDvBlocks];
+#pragma unroll
+                for (int d = 0; d < kDvBlocks; d++) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+                // V^T reads: tile j's dims 128 vt + 16 d + col, tokens 8g4 + 0..7 (lane); the 8
+                // reads of the next tile go out before the barrier (the tile is in LDS since the
+                // top of this iteration)
+                // (the base is made opaque, so that the reads become base + immediate offset and
+                // the compiler does not hoist a register per read)
+                auto vbase = [&](int t) {
+                    uint32_t x = lds_addr(raw[t % kRawSlots]) + pv_off + 128 * vt;
+                    asm volatile("" : "+v"(x));
+                    return (PA_LDS uint8_t *)(uintptr_t)x;
+                };
+                auto rd = [&](PA_LDS uint8_t *vb, int d) {
+                    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2 *)(vb + 16 * d));
+                };
+                // V^T of the tile: blocks 0 and 1 read before the barrier, block d + 2 while the
+                // MFMAs of block d run; A = V^T converted one block ahead
+                i32x2 vw[3];
+                for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
+                    const TileLoads ld = tile_top(i);
+                    // (sparse: the token addresses take two lookups each; spread over the MFMAs
+                    // they would need more registers than the wave has, so they go out here)
+                    if (i == 0 || SPARSE) {
+#pragma unroll
+                        for (int tt = 0; tt < kTokPerWave; tt++) dma_token(ld, tt);
+                    }
+                    if (i > 0) {
+                        const int j = i - 1;
+                        PA_LDS uint8_t *vb = vbase(j);
+                        // the tile's factors for O^T and the B operands (P^T of head block hb
+                        // times value tile vt's token scales, from the score waves of hb)
+                        bf16x8 pbt[4];
+#pragma unroll
+                        for (int hb = 0; hb < 4; hb++) pbt[hb] = s_p[j & 1][hb][vt][lane];
+                        {
+                            float alpha[4];
+#pragma unroll
+                            for (int hb = 0; hb < 4; hb++) alpha[hb] = s_alpha[j & 1][hb][col];
+                            if (__any(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
+                                mfma_acc_drain(acc);             // rare: a reference moved
+#pragma unroll
+                                for (int d = 0; d < kDvBlocks; d++) acc[d] = acc[d] * alpha[d & 3];
+                                mfma_acc_drain(acc);             // (wait states before the MFMAs)
+                            }
+                        }
+                        vw[2] = rd(vb, 2);
+                        bf16x8 va[2];
+                        va[0] = fp8x8_to_bf16((uint32_t)vw[0][0], (uint32_t)vw[0][1]);
+                        asm volatile("s_nop 1" : "+v"(va[0]));
 #pragma unroll
                         for (int d = 0; d < kVBlocks; d++) {
 #pragma unroll
-                            for (int e = 0; e < 4; e++) store_shared(orow + 16 * d + e, acc[4 * d + hb][e] * inv);
+                            for (int hb = 0; hb < 4; hb++) mfma_acc(acc[4 * d + hb], va[d & 1], pbt[hb]);
+                            if (!SPARSE) dma_token(ld, d); // token d of tile i + kAhead
+                            if (d + 3 < kVBlocks) vw[d % 3] = rd(vb, d + 3);
+                            if (d + 1 < kVBlocks) {
+                                va[(d + 1) & 1] = fp8x8_to_bf16((uint32_t)vw[(d + 1) % 3][0], (uint32_t)vw[(d + 1) % 3][1]);
+                                // wait states between this VALU write and the next block's MFMAs,
+                                // which the compiler does not see (asm)
+                                asm volatile("s_nop 1" : "+v"(va[(d + 1) & 1]));
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                    } else {
-#pragma unroll
-                        for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
+                    }
+                    end_tile(i + kAhead);
+                    if (i < ntiles) {
+                        PA_LDS uint8_t *vbn = vbase(i);
+                        vw[0] = rd(vbn, 0);
+                        vw[1] = rd(vbn, 1);
                     }
                 }
-            }
+                mfma_acc_drain(acc);
+                lds_barrier();                                   // both halves' sums
+                lds_barrier();                                   // s_inv in
+                // ---- epilogue: rows of head block hb: draft token and heads as in the score wave
+                // (the lane's column is made opaque here, so that the row addresses are worked
+                // out per item instead of being kept, and spilled, across the whole loop)
+                int ecol = col;
+                asm volatile("" : "+v"(ecol));
+#pragma unroll
+                for (int hb = 0; hb < 4; hb++) {
+                    const int r0 = group * kHeadsPerWG + hb * kHeadsPerWave;
+                    if (r0 >= G * nq) continue;                  // no query rows
+                    const int q_i = r0 / G;
+                    const int64_t row = (int64_t)q_i * Hq + (r0 - q_i * G) + ecol;
+                    const float inv = s_inv[hb][ecol];
+                    if (flags & 1) {
+                        uint16_t *orow = a.out + ((int64_t)b * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
+#pragma unroll
+                        for (int d = 0; d < kVBlocks; d++) {
+                            bf16x4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; e++) o[e] = (__bf16)(acc[4 * d + hb][e] * inv);
+                            *(bf16x4 *)(orow + 16 * d) = o;
+                        }
+                    } else {
+                        float *orow = a.ws_o + ((int64_t)it * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
+                        if (!SPARSE && a.counters) {         // merged inside this launch
+#pragma unroll
+                            for (int d = 0; d < kVBlocks; d++) {
+#pragma unroll
+                                for (int e = 0; e < 4; e++) store_shared(orow + 16 * d + e, acc[4 * d + hb][e] * inv);
+                            }
+                        } else {
+#pragma unroll
+                            for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
+                        }
+                    }
+                }
+            lds_barrier();                                   // the item's LDS is free
         }
-        wait_vmcnt<0>();
-        lds_barrier();                                       // the item's LDS is free
     }
     // fused combine (dense, one query token: the head group is heads [64 group, 64 group +
-    // 64)): the last workgroup to finish a request's chunks merges them
+    // 64)): the last workgroup to finish a request's chunks merges them, one unit per
+    // thread and pass (768 threads; more units would need more registers than the waves have)
     if (!SPARSE && a.counters)
-        fused_combine_tail(a, plan, part, ib, ie, group, ngroups, group * kHeadsPerWG,
+        fused_combine_tail<1>(a, plan, part, ib, ie, group, ngroups, group * kHeadsPerWG,
                            min(kHeadsPerWG, G - group * kHeadsPerWG), 1, &s_flag);
 }
 

@@ -279,8 +279,8 @@ def test_mla_config_full():
 
 def test_mla_q_dynamic_range():
     """Query rows whose 128-dim latent tiles span many binades, with outliers, tiny values,
-    zeros, an all-zero tile and an all-zero head: the kernel's split of the bf16 query
-    into two scaled fp8 terms must still give the oracle's result."""
+    zeros, an all-zero tile and an all-zero head: the bf16 score MFMAs and the fp32
+    tile-scale combination must still give the oracle's result."""
     case = _mla_case(lens=(700, 64, 1), G=32, P=64)
     B, Hq = case["B"], case["Hkv"] * case["G"]
     rng = np.random.default_rng(5)

@@ -10,8 +10,7 @@ pa_decode_run rejects; the rejections themselves are host tests in test_abi.py):
 * the smallest and largest page sizes (16 and 256 tokens) in one case each;
 * logits in the thousands (query x 20, softmax scale 1): the running maximum moves by far
   more than the exponent range between tiles, which the rescale and the MLA kernel's lazily
-  moved reference must absorb (the MLA lse bar there follows from its fp8 MFMA
-  accumulation, see below).
+  moved reference must absorb.
 
 Each result is compared element by element with the oracle at the parity bar of the
 other GPU tests (|out diff| <= 1e-2 max|V|, |lse diff| <= 1e-3); the plan words of the
@@ -137,40 +136,13 @@ def test_extreme_logits_parity(fmt):
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
-# The MLA scores come from scaled fp8 MFMAs 16x16x128, each summing 128 exact products in
-# fp32; with truncating accumulation that is an absolute error up to 128 * 2^-23 = 2^-16
-# times the sum of the products' magnitudes.  The lse follows the largest scores, so a
-# row's bar is 1e-3 + 2^-16 max over its 8 largest-score tokens of sum_d |q_d k_d|.  At the
-# configured logits that term is ~1e-5, far inside the 1e-3 bar; here (|lse| ~ 2000) it
-# is ~0.1 (out keeps the usual bar).
-MLA_ACC_REL = 2.0 ** -16
-
-
-def _mla_lse_bars(case, scale):
-    from test_oracle import dense_kv
-    G, nq = case["G"], case["q_len"]
-    bars = np.full((case["B"], G), np.inf)
-    q = (case["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)   # [B, G, 576]
-    for b in range(case["B"]):
-        if case["seq_lens"][b] == 0:
-            continue
-        K, _ = dense_kv(case, b, 0)
-        s = q[b] @ K.T * scale                                   # [G, L]
-        top = np.argsort(-s, axis=1)[:, :8]
-        mag = np.abs(q[b])[:, None, :] * np.abs(K[top])          # [G, 8, 576]
-        bars[b] = 1e-3 + MLA_ACC_REL * scale * mag.sum(-1).max(-1)
-    return bars
-
-
 def test_mla_extreme_logits_parity():
+    """Logits in the thousands (query x 20, scale 1) on the MLA-656 path, at the plain bar:
+    the scores run on bf16 MFMAs (exact products, fp32 sums) with the per-token tile scales
+    applied in fp32, so their error stays a few fp32 roundings of the score."""
     case = _mla_case((900, 5, 2100), G=32, splits=0)
     _scale_q(case, 20.0)
     out, lse = DecodeRun(case)(scale=1.0)
     ref_out, ref_lse = oracle.decode(case, scale=1.0)
     assert np.max(np.abs(ref_lse)) > 500.0
-    assert_parity(case, out, ref_lse, ref_out, ref_lse)     # out; lse below
-    fin = np.isfinite(ref_lse)
-    assert np.array_equal(np.isfinite(lse), fin)
-    err = np.abs(lse - np.where(fin, ref_lse, 0.0))
-    bars = _mla_lse_bars(case, 1.0)
-    assert np.all(err[fin] <= bars[fin]), (err[fin].max(), bars[fin].min())
+    assert_parity(case, out, lse, ref_out, ref_lse)
