@@ -109,7 +109,8 @@ pa_status num_parts_for(const pa_decode_desc *d, int *np)
         const int wgs_per_cu = PA_WGS_PER_CU;
         n = (cu * wgs_per_cu + d->Hkv - 1) / d->Hkv;
     }
-    *np = n < 1 ? 1 : n;
+    // (the plan kernel keeps the per-part prefix in LDS: at most kMaxPlanParts parts)
+    *np = n < 1 ? 1 : (n > pa::kMaxPlanParts ? pa::kMaxPlanParts : n);
     return PA_OK;
 }
 

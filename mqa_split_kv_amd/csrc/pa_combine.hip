@@ -7,7 +7,10 @@
 namespace pa {
 namespace {
 
-constexpr int kCombineThreads = 256;
+// one wave per workgroup: a (request, KV head)'s rows spread over several small workgroups,
+// every lane busy (HD64: 128 units of 4 dims per (request, head) -> 2 workgroups), so that
+// the partial loads of all of them are in flight on more compute units at once
+constexpr int kCombineThreads = 64;
 
 __global__ __launch_bounds__(kCombineThreads) void pa_combine_kernel(
     const int32_t *__restrict__ plan, const float *__restrict__ ws_o,

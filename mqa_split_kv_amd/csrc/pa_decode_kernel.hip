@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     // fused combine: the last workgroup to finish a request's chunks merges them
     if (a.counters)
-        fused_combine_tail(a, plan, part, ib, ie, h, a.Hkv, h * G, G, gridDim.z, &s_flag);
+        fused_combine_tail<2>(a, plan, part, ib, ie, h, a.Hkv, h * G, G, gridDim.z, &s_flag);
 }
 
 }  // namespace

@@ -16,6 +16,7 @@ constexpr int kTileTokens = 64;
 constexpr int kPlanMagic = 0x50414450;
 constexpr int kPlanHeaderWords = 8;
 constexpr int kMaxBatch = 4096;       // plan kernel keeps per-request prefix sums in LDS
+constexpr int kMaxPlanParts = 1024;   // and the balanced rule's per-part prefix
 
 // Plan buffer (int32 words):
 //   [0] magic  [1] mode (0 fixed splits, 1 balanced)  [2] B  [3] num_parts

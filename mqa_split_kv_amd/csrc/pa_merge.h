@@ -26,7 +26,7 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 // output out[(b * nq * Hq + qr) * Dv ...], lse[b * nq * Hq + qr].  Merges heads
 // [hq0, hq0 + nrows) of every query token of request b from chunks c0 .. c0 + n - 1.  A
 // work unit is one (query token, head) row and 4 dims; thread tid takes units tid, tid + nthr, ... kUnits at a
-// time (1 in the wide combine grid, 4 in a single fused-combine workgroup), and reads the
+// time (1 in the wide combine grid, 1 to 4 in a single fused-combine workgroup), and reads the
 // chunks kChunkBatch at a time with a running maximum (the same rescaling as the online
 // softmax), so that up to kUnits x kChunkBatch partial loads are in flight instead of one
 // dependent load after another.  A unit's arithmetic does not depend on kUnits, so both
@@ -36,7 +36,7 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 // attention sink (sinks[hq], natural-log units, or null) joins once as one more partial
 // with lse = sink and O = 0 (XQA article, section "一个容易漏掉的细节: attention sink":
 // the final reduction adds the sink to the denominator).
-constexpr int kChunkBatch = 4;
+constexpr int kChunkBatch = 8;
 
 // Partials shared across workgroups inside one launch (the fused combine) are written and
 // read with agent-scope relaxed atomics: on gfx950 such stores and loads are coherent at

@@ -17,7 +17,7 @@
 namespace pa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 512;
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
@@ -34,31 +34,50 @@ struct Span {
     __device__ int tiles(int L) const { return ceil_div_i(len(L), kTileTokens) - first(L); }
 };
 
-// Exclusive scan of `n` ints in LDS (in place), returns the total.  All threads call.
-__device__ int block_exclusive_scan(int *v, int n, int *scratch)
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// inclusive scan of x across the 64 lanes of a wave: DPP row shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row broadcasts of lanes 15 and 31 (lanes a shift or
+// broadcast does not reach add 0)
+__device__ __forceinline__ int wave_inclusive_scan(int x)
 {
-    const int tid = threadIdx.x;
-    const int per = ceil_div_i(n, kPlanThreads);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+// Exclusive scan of v[0..n) in LDS, in place; v[n] = the total, which is also returned.
+// Each thread sums a run of ceil(n / kPlanThreads) elements, the runs are scanned within
+// each wave and across the waves (by one wave): two barriers.  All threads call.
+__device__ int block_exclusive_scan(int *v, int n, int *wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int per = (n + kPlanThreads - 1) / kPlanThreads;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int s = 0;
     for (int i = lo; i < hi; i++) s += v[i];
-    scratch[tid] = s;
+    const int incl = wave_inclusive_scan(s);
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    // Hillis-Steele inclusive scan over the per-thread sums
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        int x = tid >= off ? scratch[tid - off] : 0;
-        __syncthreads();
-        scratch[tid] += x;
-        __syncthreads();
+    if (w == 0) {
+        const int x = lane < kPlanWaves ? wsum[lane] : 0;
+        const int y = wave_inclusive_scan(x);
+        if (lane < kPlanWaves) wsum[kPlanWaves + lane] = y - x;       // exclusive wave offsets
+        if (lane == kPlanWaves - 1) wsum[2 * kPlanWaves] = y;          // total
     }
-    int run = scratch[tid] - s;
+    __syncthreads();
+    int run = wsum[kPlanWaves + w] + incl - s;
     for (int i = lo; i < hi; i++) {
-        int x = v[i];
+        const int x = v[i];
         v[i] = run;
         run += x;
     }
-    __syncthreads();
-    int total = scratch[kPlanThreads - 1];
+    const int total = wsum[2 * kPlanWaves];
+    if (tid == 0) v[n] = total;
     __syncthreads();
     return total;
 }
@@ -69,8 +88,10 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
     int counters_off, int n_counters, Span sp)
 {
     __shared__ int s_start[kMaxBatch + 1];   // tile prefix S_b
-    __shared__ int s_ne[kMaxBatch + 1];      // non-empty request prefix
-    __shared__ int s_scratch[kPlanThreads];
+    __shared__ int s_chunk[kMaxBatch + 1];   // chunk prefix (chunk_off)
+    __shared__ int s_part[kMaxPlanParts + 1];   // item prefix per part (part_begin)
+    __shared__ int s_len[kMaxBatch];         // seq_lens
+    __shared__ int s_wsum[2 * kPlanWaves + 1];
     const int tid = threadIdx.x;
     int32_t *part_begin = plan + part_begin_off;
     int32_t *chunk_off = plan + chunk_off_off;
@@ -106,131 +127,73 @@ __global__ __launch_bounds__(kPlanThreads) void pa_plan_kernel(
         return;
     }
 
-    // ---- balanced parts
+    // ---- balanced parts: tile counts and their prefix (everything stays in LDS)
     for (int b = tid; b < B; b += kPlanThreads) {
-        const int n = sp.tiles(seq_lens[b]);
-        s_start[b] = n;
-        s_ne[b] = n > 0 ? 1 : 0;
+        const int L = seq_lens[b];
+        s_len[b] = L;
+        s_start[b] = sp.tiles(L);
     }
+    for (int p = tid; p <= num_parts; p += kPlanThreads) s_part[p] = 0;
     __syncthreads();
-    const int N = block_exclusive_scan(s_start, B, s_scratch);
-    const int NE = block_exclusive_scan(s_ne, B, s_scratch);
-    if (tid == 0) { s_start[B] = N; s_ne[B] = NE; }
-    __syncthreads();
+    const int N = block_exclusive_scan(s_start, B, s_wsum);
 
-    const int64_t Np = num_parts;
-    // first tile of part p
-    auto edge = [&](int p) -> int { return (int)(((int64_t)p * N) / Np); };
-    // part containing global tile x (0 <= x < N): largest p with edge(p) <= x
-    auto part_of = [&](int x) -> int { return (int)((((int64_t)x + 1) * Np - 1) / N); };
-    // request containing global tile x: largest b with S_b <= x (it is non-empty)
-    auto req_of = [&](int x) -> int {
-        int lo = 0, hi = B;                  // S_lo <= x < S_hi
-        while (hi - lo > 1) {
-            int mid = (lo + hi) >> 1;
-            if (s_start[mid] <= x) lo = mid; else hi = mid;
-        }
-        return lo;
-    };
+    // Part p owns global tiles [edge(p), edge(p + 1)), edge(p) = floor(p N / P); the part
+    // holding tile x (0 <= x < N) is the largest p with edge(p) <= x, floor(((x + 1) P - 1) / N).
+    // Both in double: the numerators stay below 2^53 and the quotients' fractional parts are
+    // multiples of 1 / P or 1 / N, far above the rounding error, so the floors are exact.
+    const int P = num_parts;
+    auto edge = [&](int p) -> int { return (int)(((double)p * (double)N) / (double)P); };
+    auto part_of = [&](int x) -> int { return (int)(((double)(x + 1) * (double)P - 1.0) / (double)N); };
+    // When N >= P every part holds at least one tile, so the parts a request touches are
+    // consecutive and all non-empty: one chunk per part.  Otherwise every non-empty part
+    // holds exactly one tile and a request has one chunk per tile.
+    const bool wide = N >= P;
 
-    // items per part -> part_begin (exclusive scan over parts, in global memory)
-    // parts are processed in strided chunks; the count is kept in part_begin first.
-    for (int p = tid; p < num_parts; p += kPlanThreads) {
-        const int e0 = edge(p), e1 = edge(p + 1);
-        int cnt = 0;
-        if (e1 > e0) {
-            const int bf = req_of(e0), bl = req_of(e1 - 1);
-            cnt = s_ne[bl + 1] - s_ne[bf];
-        }
-        part_begin[p] = cnt;
-    }
-    __threadfence_block();
-    __syncthreads();
-    // exclusive scan of part_begin[0..num_parts) in global memory, by the whole block
-    {
-        const int per = ceil_div_i(num_parts, kPlanThreads);
-        const int lo = min(num_parts, tid * per), hi = min(num_parts, lo + per);
-        int s = 0;
-        for (int i = lo; i < hi; i++) s += part_begin[i];
-        s_scratch[tid] = s;
-        __syncthreads();
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
-            int x = tid >= off ? s_scratch[tid - off] : 0;
-            __syncthreads();
-            s_scratch[tid] += x;
-            __syncthreads();
-        }
-        int run = s_scratch[tid] - s;
-        for (int i = lo; i < hi; i++) {
-            int x = part_begin[i];
-            part_begin[i] = run;
-            run += x;
-        }
-        if (tid == 0) part_begin[num_parts] = s_scratch[kPlanThreads - 1];
-    }
-    __threadfence_block();
-    __syncthreads();
-
-    // chunks per request -> chunk_off
+    // chunks per request; each chunk counts one item of its part
     for (int b = tid; b < B; b += kPlanThreads) {
-        const int n = s_start[b + 1] - s_start[b];
-        // When N >= num_parts every part holds at least one tile, so the parts a request
-        // touches are consecutive and all non-empty.  Otherwise every non-empty part holds
-        // exactly one tile and the request has one chunk per tile.
+        const int S = s_start[b], n = s_start[b + 1] - S;
         int nch = 0;
-        if (n > 0)
-            nch = (int64_t)N >= Np ? part_of(s_start[b] + n - 1) - part_of(s_start[b]) + 1 : n;
-        chunk_off[b] = nch;
-    }
-    __threadfence_block();
-    __syncthreads();
-    {
-        const int per = ceil_div_i(B, kPlanThreads);
-        const int lo = min(B, tid * per), hi = min(B, lo + per);
-        int s = 0;
-        for (int i = lo; i < hi; i++) s += chunk_off[i];
-        s_scratch[tid] = s;
-        __syncthreads();
-        for (int off = 1; off < kPlanThreads; off <<= 1) {
-            int x = tid >= off ? s_scratch[tid - off] : 0;
-            __syncthreads();
-            s_scratch[tid] += x;
-            __syncthreads();
+        if (n > 0) {
+            const int pf = part_of(S);
+            nch = wide ? part_of(S + n - 1) - pf + 1 : n;
+            for (int j = 0; j < nch; j++) atomicAdd(&s_part[wide ? pf + j : part_of(S + j)], 1);
         }
-        int run = s_scratch[tid] - s;
-        for (int i = lo; i < hi; i++) {
-            int x = chunk_off[i];
-            chunk_off[i] = run;
-            run += x;
-        }
-        if (tid == 0) chunk_off[B] = s_scratch[kPlanThreads - 1];
+        s_chunk[b] = nch;
     }
-    __threadfence_block();
     __syncthreads();
+    const int n_items = block_exclusive_scan(s_part, P, s_wsum);
+    block_exclusive_scan(s_chunk, B, s_wsum);
+    for (int p = tid; p <= P; p += kPlanThreads) part_begin[p] = s_part[p];
+    for (int b = tid; b <= B; b += kPlanThreads) chunk_off[b] = s_chunk[b];
 
-    // items of each part, in request order
-    for (int p = tid; p < num_parts; p += kPlanThreads) {
-        const int e0 = edge(p), e1 = edge(p + 1);
-        if (e1 <= e0) continue;
-        int k = part_begin[p];
-        const int bf = req_of(e0), bl = req_of(e1 - 1);
-        for (int b = bf; b <= bl; b++) {
-            const int S = s_start[b], n = s_start[b + 1] - S;
-            if (n == 0) continue;
-            const int f = sp.first(seq_lens[b]);
-            const int lo = f + max(e0, S) - S, hi = f + min(e1, S + n) - S;
-            const int L = sp.len(seq_lens[b]);
-            const int nch = chunk_off[b + 1] - chunk_off[b];
-            items[4 * k + 0] = b;
-            items[4 * k + 1] = lo * kTileTokens;
-            items[4 * k + 2] = min(hi * kTileTokens, L);
-            items[4 * k + 3] = nch == 1 ? 1 : 0;
-            k++;
+    // items: items are numbered in (request, part) order along the tile axis, so chunk j of
+    // request b is item chunk_off[b] + j
+    for (int b = tid; b < B; b += kPlanThreads) {
+        const int S = s_start[b], n = s_start[b + 1] - S;
+        if (n == 0) continue;
+        const int L = s_len[b];
+        const int f = sp.first(L), Lk = sp.len(L);
+        const int c0 = s_chunk[b], nch = s_chunk[b + 1] - c0;
+        const int pf = wide ? part_of(S) : 0;
+        for (int j = 0; j < nch; j++) {
+            int lo, hi;                                  // global tiles of the chunk
+            if (wide) {
+                lo = max(edge(pf + j), S);
+                hi = min(edge(pf + j + 1), S + n);
+            } else {
+                lo = S + j;
+                hi = lo + 1;
+            }
+            int32_t *it = items + 4 * (c0 + j);
+            it[0] = b;
+            it[1] = (f + lo - S) * kTileTokens;
+            it[2] = min((f + hi - S) * kTileTokens, Lk);
+            it[3] = nch == 1 ? 1 : 0;
         }
     }
     if (tid == 0) {
-        plan[0] = kPlanMagic; plan[1] = 1; plan[2] = B; plan[3] = num_parts;
-        plan[4] = part_begin[num_parts]; plan[5] = kTileTokens; plan[6] = max_items; plan[7] = 0;
+        plan[0] = kPlanMagic; plan[1] = 1; plan[2] = B; plan[3] = P;
+        plan[4] = n_items; plan[5] = kTileTokens; plan[6] = max_items; plan[7] = 0;
     }
 }
 
