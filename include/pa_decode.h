@@ -245,8 +245,9 @@ pa_status pa_decode_noalloc(const pa_decode_desc *desc, const void *q, const voi
    on the current device (B * num_splits, or the balanced part count). */
 pa_status pa_decode_num_parts(const pa_decode_desc *desc, int32_t *num_parts);
 
-/* Static string for a status code. */
-const char *pa_status_string(pa_status s);
+/* Static string for a status code (a pa_status value; any other int gives "unknown status").
+   The parameter is an int, not the enum type, so that any value a caller passes is valid. */
+const char *pa_status_string(int status);
 
 #ifdef __cplusplus
 }

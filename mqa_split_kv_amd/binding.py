@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "lib", "libpa_decode.so")
+# PA_DECODE_LIB selects another build of the same library (the host-sanitizer build of
+# `python -m mqa_split_kv_amd.build --sanitize`, for the CPU checks that run under ASan/UBSan)
+LIB_PATH = os.environ.get("PA_DECODE_LIB") or os.path.join(HERE, "lib", "libpa_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_SIZE, PA_ERR_DEVICE = range(5)

@@ -61,6 +61,43 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
+SAN_LIB = os.path.join(LIBDIR, "libpa_decode_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libpa_decode_san.so: the library with its host-side code (argument validation, size
+    queries, launches in pa_api.cpp) built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (the device code is unchanged).  It runs only with clang's ASan runtime preloaded."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "pa_api.cpp":
+            obj = os.path.join(OBJDIR, "pa_api_san.o")
+            cmd = [hipcc()] + common_flags() + SAN_FLAGS + ["-g", "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+            if not os.path.exists(obj):
+                obj = _compile(src)
+            objs.append(obj)
+    tmp = SAN_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Build libpa_decode.so (the decode path) and libpa_probe.so (measurement helpers)."""
     os.makedirs(OBJDIR, exist_ok=True)
@@ -76,5 +113,8 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

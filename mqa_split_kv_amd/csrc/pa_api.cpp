@@ -247,7 +247,7 @@ pa_status launch_combine_for(const pa_decode_desc *desc, const PlanLayout &L, co
 
 extern "C" {
 
-const char *pa_status_string(pa_status s)
+const char *pa_status_string(int s)
 {
     switch (s) {
     case PA_OK: return "ok";

@@ -21,7 +21,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects another build of oracle.c (build(sanitize=True): ASan + UBSan, for the
+# pins run under the sanitizers)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
 
 KV_BF16, KV_FP8_PAGE_HEAD, KV_MLA656 = 0, 1, 2
 
@@ -38,15 +41,21 @@ class _Desc(ctypes.Structure):
     ]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call([
-            "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, no fast-math, no FP contraction), or
+    with sanitize=True into liboracle_san.so (AddressSanitizer + UndefinedBehaviorSanitizer,
+    aborting on the first report; load it with the sanitizer runtimes preloaded)."""
+    out = _SAN_LIB_PATH if sanitize else _LIB_PATH
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        flags = ["-O2"] if not sanitize else ["-O1", "-g", "-fsanitize=address,undefined",
+                                              "-fno-sanitize-recover=undefined",
+                                              "-fno-omit-frame-pointer"]
+        subprocess.check_call(["gcc"] + flags + [
+            "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
             "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
