@@ -285,6 +285,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     // The two roles run the same items with the same barrier sequence, each in its own
     // loop (values one role keeps across its items then never occupy the other's registers).
     if (scorer) {
+        // issue priority on the SIMD (oldest wave first by default): value wave, then score
+        // half 1, then score half 0; measured -5 % kernel time on the MLA workload
+        if (sb) __builtin_amdgcn_s_setprio(1);
         for (int it = ib; it < ie; it++) {
             const int b = plan[a.items_off + 4 * it + 0];
             const int t0 = plan[a.items_off + 4 * it + 1];
@@ -517,13 +520,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             lds_barrier();                                   // the item's LDS is free
         }
     } else {
+        // the value wave issues first on its SIMD (its 32 MFMAs and the tile loads are the
+        // longest chain of the three), then the later score half
+        __builtin_amdgcn_s_setprio(2);
         for (int it = ib; it < ie; it++) {
             const int b = plan[a.items_off + 4 * it + 0];
             const int t0 = plan[a.items_off + 4 * it + 1];
             const int t1 = plan[a.items_off + 4 * it + 2];
             const int flags = plan[a.items_off + 4 * it + 3];
             const int ntiles = (t1 - t0 + kT - 1) / kT;
-            const int64_t qr = (int64_t)qi * Hq + head0 + col;     // query row within the request
 
             const int lw = wave - kScoreWaves;               // loader index
             // ---- lookups.  Sparse: lane l < 8 loads those of token l of the wave's 8 in tile
