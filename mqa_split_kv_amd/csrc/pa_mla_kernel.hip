@@ -37,8 +37,9 @@
 // Per 32-token tile:
 //   * the tokens' 656 bytes go HBM -> LDS by direct-to-LDS loads (one instruction per
 //     token, 41 lanes of 16 bytes; a token that is not real reads as zeros) into a 5-slot
-//     ring of 752-byte rows; each score wave loads 4 tokens; tile i+3's loads go out at the
-//     top of iteration i, after the wait for tiles i and i+1 (the score waves read tile
+//     ring of 21,856-byte tile slots (token rows placed for conflict-free reads, raw_row);
+//     each value wave loads 8 tokens, tile i+3's one per 16-dim block of its PV MFMAs in
+//     iteration i (tiles i and i+1 are waited for at its top: the score waves read tile
 //     i+1's keys).  Page ids come the same way, 3 tiles ahead, into a small LDS ring (a
 //     scalar load would make every later LDS wait also wait for it);
 //   * scores: per 128-dim scale tile u, four bf16 MFMAs 16x16x32 on the codes converted
@@ -105,8 +106,12 @@ constexpr int kChunks = kTokBytes / 16;            // 41 16-byte chunks per toke
 constexpr int kT = 32;                             // tokens per tile
 constexpr int kLoadWaves = kValueWaves;           // the value waves issue the tile loads
 constexpr int kTokPerWave = kT / kLoadWaves;       // 8 tokens loaded per value wave and tile
-constexpr int kRawRow = 752;                       // LDS row of a token (656 + 96)
-constexpr int kRawTile = kT * kRawRow;             // 24064
+// LDS placement of a tile's 32 token rows (see raw_row): groups of 4 consecutive tokens,
+// rows 672 bytes apart inside a group; group j starts at kGroupQuad[j] 16-byte units
+constexpr int kRowStep = 672;                      // bytes between the rows of a group
+constexpr int kGroupQuad[8] = {0, 167, 344, 511, 688, 855, 1032, 1199};
+constexpr int kHalfGroupBytes = 167 * 16;          // from token 0 to token 4 of a wave's 8
+constexpr int kRawTile = (1199 + 3 * 42 + 41) * 16;   // 21856: the last row's end
 constexpr int kRawSlots = 5;                       // tile ring
 constexpr int kAhead = kRawSlots - 2;              // loads go out 3 tiles ahead (2 ahead of the keys'
                                                    // first use); lookups: page ids 3 (sparse:
@@ -121,6 +126,29 @@ static_assert(kTokPerWave == 128 / 16, "a value wave issues one token load per 1
 static_assert(kLookRing > 2 * kAhead && (kLookRing & (kLookRing - 1)) == 0, "lookup ring");
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// LDS byte offset of token row r (0..31) in a tile slot.  LDS has 64 four-byte banks; a
+// 16-byte read serves 16 lanes per cycle, lanes {0-3, 12-15, 20-23, 24-27} together and
+// {4-11, 16-19, 28-31} together (then the same for lanes 32-63), an 8-byte read lanes 0-31,
+// then 32-63 (both measured on MI355X, lane pair by lane pair).  A score wave's operand read
+// takes, in lane quad 4 g4 + c, the rows of group 2c + sb at column 16 g4; the transposed
+// value read takes rows 8 g4 + 0..7.  With group j's 4 rows 42 16-byte units apart (bank
+// groups p_j + {0, 10, 4, 14} mod 16), both are conflict-free when the group starts sit at
+// bank groups p0 = p4 = 0, p2 = p6 = 8 (row block 0) and p1 = p5 = 7, p3 = p7 = 15 (row
+// block 1): each cycle's 16 rows then cover all 16 bank groups (counted with
+// SQ_LDS_BANK_CONFLICT on MI355X: 0 for both reads, where 752-byte rows had a 2-way
+// conflict on the operand reads).  The groups are packed into 21,856 bytes.
+__device__ __forceinline__ int raw_row(int r)
+{
+    const int k = r >> 3;                          // pair of groups (2k, 2k + 1)
+    return (k == 0 ? 0 : k == 1 ? 344 * 16 : k == 2 ? 688 * 16 : 1032 * 16) + ((r >> 2) & 1) * kHalfGroupBytes +
+           (r & 3) * kRowStep;
+}
+static_assert(kGroupQuad[1] - kGroupQuad[0] == 167 && kGroupQuad[3] - kGroupQuad[2] == 167 &&
+              kGroupQuad[5] - kGroupQuad[4] == 167 && kGroupQuad[7] - kGroupQuad[6] == 167 &&
+              kGroupQuad[2] == 344 && kGroupQuad[4] == 688 && kGroupQuad[6] == 1032,
+              "raw_row and the loads place the second 4 tokens of each 8 at a fixed distance");
+static_assert(kGroupQuad[7] * 16 + 3 * kRowStep + kTokBytes <= kRawTile, "last row inside the slot");
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool SPARSE>
@@ -237,9 +265,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     constexpr int kLoadsPerTile = MlaCfg<SPARSE>::kLoadsPerTile;
     __shared__ __attribute__((aligned(16))) uint8_t raw[kRawSlots][kRawTile];
     // the PV B operands of a tile from the score waves of head block hg, in their lanes'
-    // layout (lane (col, g4): head col, tokens 8g4 + 0..7, row block sb's 4 in bytes 8sb ..
-    // 8sb+7): P^T times value tile t's token scales, bf16: [tile parity][hg][value tile t][lane]
-    __shared__ bf16x8 s_p[2][4][4][64];
+    // layout (lane (col, g4): head col, tokens 8g4 + 0..7, of which row block sb holds
+    // 8g4 + 4sb + 0..3): P^T times value tile t's token scales, bf16, [tile parity][hg]
+    // [value tile t][sb][lane]; each score wave writes 512 contiguous bytes (a half-slot
+    // write per lane, 16 bytes apart, would meet the same banks four times)
+    __shared__ bf16x4 s_p[2][4][4][2][64];
     __shared__ float s_alpha[2][4][16];       // factor on O^T before the tile's PV, per head
     __shared__ float s_tmax[2][2][4][16];     // [tile parity][sb][hg][head]: half-tile maxima
     __shared__ float s_lsum[2][4][16];        // [sb][hg][head]: the halves' row sums
@@ -273,10 +303,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     // rope operand, the scale rows of this lane's tokens 8g4 + 4sb + r, and the transposed
     // PV read (lane pair 2r, 2r+1 of a 16-lane block supplies row 8g4 + r, bytes 0-7 and
     // 8-15 of the block's 16 value dims)
-    const uint32_t qk_off = (uint32_t)((8 * (col >> 2) + 4 * sb + (col & 3)) * kRawRow + 16 * g4);
+    // (the scale rows 8g4 + 4sb + 0..3 are one group of 4, kRowStep apart)
+    const uint32_t qk_off = (uint32_t)(raw_row(8 * (col >> 2) + 4 * sb + (col & 3)) + 16 * g4);
     const uint32_t rope_off = qk_off + 528;
-    const uint32_t sc_off = (uint32_t)((8 * g4 + 4 * sb) * kRawRow + 512);
-    const uint32_t pv_off = (uint32_t)((8 * g4 + ((lane & 15) >> 1)) * kRawRow + 8 * (lane & 1));
+    const uint32_t sc_off = (uint32_t)(raw_row(8 * g4 + 4 * sb) + 512);
+    const uint32_t pv_off = (uint32_t)(raw_row(8 * g4 + ((lane & 15) >> 1)) + 8 * (lane & 1));
 
     // a fixed-split plan has exactly one item per part (no plan read on the critical path)
     const int ib = a.fixed_splits > 0 ? part : plan[a.part_begin_off + part];
@@ -360,7 +391,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     auto rd_scales = [&](int u) {
 #pragma unroll
                         for (int r = 0; r < 4; r++)
-                            scu[u & 1][r] = *(PA_LDS const float *)(slot + sc_off + r * kRawRow + 4 * u);
+                            scu[u & 1][r] = *(PA_LDS const float *)(slot + sc_off + r * kRowStep + 4 * u);
                     };
                     kc[0] = rd_codes(0);
                     bf16x8 av[2];
@@ -463,7 +494,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         // scales), from the scale rows read again one step before their use (row
                         // q read in step 5 + q into scr[q & 1], used in step 6 + q)
                         if (s >= 5 && s < 9)
-                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + (s - 5) * kRawRow);
+                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + (s - 5) * kRowStep);
                         if (s >= 6 && s < 10) {
                             const int r = s - 6;
 #pragma unroll
@@ -472,7 +503,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         if (s == 11 || s == 12) {
 #pragma unroll
                             for (int t = 2 * (s - 11); t < 2 * (s - 11) + 2; t++)
-                                *(bf16x4 *)((uint8_t *)&s_p[i & 1][hg][t][lane] + 8 * sb) = pb[t];
+                                s_p[i & 1][hg][t][sb][lane] = pb[t];
                         }
                         if (s == 13) {
                             // both halves hold the same factor and both write it (no branch in the
@@ -595,7 +626,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             };
             auto prep_tile = [&](int t, int page) {
                 TileLoads L;
-                L.lds0 = lds_addr(&raw[t % kRawSlots][kTokPerWave * lw * kRawRow]);
+                L.lds0 = lds_addr(&raw[t % kRawSlots][raw_row(kTokPerWave * lw)]);
                 L.tok = nullptr;
                 L.nreal = 0;
                 L.pos = L.pgv = 0;
@@ -622,17 +653,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 }
                 return L;
             };
+            // row of token tt of the wave's 8 relative to its first (two groups of 4)
+            auto tok_row = [](int tt) { return (tt >> 2) * kHalfGroupBytes + (tt & 3) * kRowStep; };
             auto dma_token = [&](const TileLoads &L, int tt) {
                 if (SPARSE) {
                     const int p = __builtin_amdgcn_readlane(L.pos, tt);
                     const int pg = __builtin_amdgcn_readlane(L.pgv, tt);
                     const bool ok = (L.nreal >> tt) & 1;
                     const uint8_t *src = a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0);
-                    if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tt * kRawRow);
+                    if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
                 } else {
                     if (lane < kChunks)
                         lds_dma_buf16(L.tok + (int64_t)tt * a.s_tok_b, tt < L.nreal ? kTokBytes : 0, 16 * lane,
-                                      L.lds0 + tt * kRawRow);
+                                      L.lds0 + tok_row(tt));
                 }
             };
             auto end_tile = [&](int t) {
@@ -719,7 +752,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         // times value tile vt's token scales, from the score waves of hb)
                         bf16x8 pbt[4];
 #pragma unroll
-                        for (int hb = 0; hb < 4; hb++) pbt[hb] = s_p[j & 1][hb][vt][lane];
+                        for (int hb = 0; hb < 4; hb++) {
+                            const bf16x4 lo = s_p[j & 1][hb][vt][0][lane], hi = s_p[j & 1][hb][vt][1][lane];
+#pragma unroll
+                            for (int k = 0; k < 4; k++) {
+                                pbt[hb][k] = lo[k];
+                                pbt[hb][4 + k] = hi[k];
+                            }
+                        }
                         {
                             float alpha[4];
 #pragma unroll
