@@ -238,7 +238,7 @@ pa_status launch_combine_for(const pa_decode_desc *desc, const PlanLayout &L, co
                                                          desc->Dv));
     if (pa::launch_combine((const int32_t *)plan, ws_o, ws_lse, sinks, (uint16_t *)out, lse, desc->B,
                            desc->Hkv, desc->G, desc->q_len, desc->Dv, L.chunk_off_off,
-                           desc->num_splits > 0 ? desc->num_splits : 0, stream) != hipSuccess)
+                           desc->num_splits > 0 ? desc->num_splits : 0, desc->kv_format, stream) != hipSuccess)
         return PA_ERR_DEVICE;
     return PA_OK;
 }

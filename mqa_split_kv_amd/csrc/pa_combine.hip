@@ -15,7 +15,8 @@ constexpr int kCombineThreads = 64;
 __global__ __launch_bounds__(kCombineThreads) void pa_combine_kernel(
     const int32_t *__restrict__ plan, const float *__restrict__ ws_o,
     const float *__restrict__ ws_lse, const float *__restrict__ sinks, uint16_t *__restrict__ out,
-    float *__restrict__ lse, int Hkv, int G, int q_len, int Dv, int chunk_off_off, int fixed_splits)
+    float *__restrict__ lse, int Hkv, int G, int q_len, int Dv, int chunk_off_off, int fixed_splits,
+    int batch)
 {
     const int bh = blockIdx.x;
     const int b = bh / Hkv, h = bh % Hkv;
@@ -23,20 +24,22 @@ __global__ __launch_bounds__(kCombineThreads) void pa_combine_kernel(
     const int c0 = fixed_splits > 0 ? b * fixed_splits : plan[chunk_off_off + b];
     const int n = fixed_splits > 0 ? fixed_splits : plan[chunk_off_off + b + 1] - c0;
     if (n == 1) return;                           // the decode kernel wrote this row
-    merge_rows<1>(ws_o, ws_lse, sinks, out, lse, b, c0, n, Hkv * G, q_len, Dv, h * G, G,
-               blockIdx.y * kCombineThreads + threadIdx.x, gridDim.y * kCombineThreads);
+    merge_rows<1>(batch, ws_o, ws_lse, sinks, out, lse, b, c0, n, Hkv * G, q_len, Dv, h * G, G,
+                  blockIdx.y * kCombineThreads + threadIdx.x, gridDim.y * kCombineThreads);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           const float *sinks, uint16_t *out, float *lse, int B, int Hkv, int G,
-                          int q_len, int Dv, int chunk_off_off, int fixed_splits, hipStream_t stream)
+                          int q_len, int Dv, int chunk_off_off, int fixed_splits, int kv_format,
+                          hipStream_t stream)
 {
     const int per_bh = q_len * G * (Dv / 4);
     const dim3 grid(B * Hkv, (per_bh + kCombineThreads - 1) / kCombineThreads);
     hipLaunchKernelGGL(pa_combine_kernel, grid, dim3(kCombineThreads), 0, stream, plan, ws_o,
-                       ws_lse, sinks, out, lse, Hkv, G, q_len, Dv, chunk_off_off, fixed_splits);
+                       ws_lse, sinks, out, lse, Hkv, G, q_len, Dv, chunk_off_off, fixed_splits,
+                       merge_batch(kv_format));
     return hipGetLastError();
 }
 

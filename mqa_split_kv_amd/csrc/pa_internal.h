@@ -107,6 +107,7 @@ hipError_t launch_append(const pa_decode_desc *d, int n_new, const void *k_new, 
                          void *v_pool, float *k_scale, float *v_scale, hipStream_t stream);
 hipError_t launch_combine(const int32_t *plan, const float *ws_o, const float *ws_lse,
                           const float *sinks, uint16_t *out, float *lse, int B, int Hkv, int G,
-                          int q_len, int Dv, int chunk_off_off, int fixed_splits, hipStream_t stream);
+                          int q_len, int Dv, int chunk_off_off, int fixed_splits, int kv_format,
+                          hipStream_t stream);
 
 }  // namespace pa

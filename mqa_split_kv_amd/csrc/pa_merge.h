@@ -27,16 +27,20 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 // [hq0, hq0 + nrows) of every query token of request b from chunks c0 .. c0 + n - 1.  A
 // work unit is one (query token, head) row and 4 dims; thread tid takes units tid, tid + nthr, ... kUnits at a
 // time (1 in the wide combine grid, 1 to 4 in a single fused-combine workgroup), and reads the
-// chunks kChunkBatch at a time with a running maximum (the same rescaling as the online
-// softmax), so that up to kUnits x kChunkBatch partial loads are in flight instead of one
-// dependent load after another.  A unit's arithmetic does not depend on kUnits, so both
-// callers produce the same bits.  The result is
+// chunks kBatch at a time with a running maximum (the same rescaling as the online
+// softmax), so that up to kUnits x kBatch partial loads are in flight instead of one
+// dependent load after another.  A unit's arithmetic does not depend on kUnits, and both
+// callers take the batch from merge_batch(), so both produce the same bits.  The result is
 //   out = sum_i exp(lse_i - M) O_i / sum_i exp(lse_i - M),  lse = M + ln sum_i exp(lse_i - M)
 // which is the merge equation above with exp(lse_i - lse) = exp(lse_i - M) / sum.  An
 // attention sink (sinks[hq], natural-log units, or null) joins once as one more partial
 // with lse = sink and O = 0 (XQA article, section "一个容易漏掉的细节: attention sink":
 // the final reduction adds the sink to the denominator).
-constexpr int kChunkBatch = 8;
+// Chunks per load round: 8 when requests are cut into many chunks (fixed splits, the
+// bf16 / fp8 balanced plans), 4 for the MLA workload's 2-3 chunks per request, where 8
+// mostly issues masked loads (measured on MI355X: combine kernel 11.3 against 12.8 us on the
+// MLA workload).
+__host__ __device__ inline int merge_batch(int kv_format) { return kv_format == PA_KV_MLA656 ? 4 : 8; }
 
 // Partials shared across workgroups inside one launch (the fused combine) are written and
 // read with agent-scope relaxed atomics: on gfx950 such stores and loads are coherent at
@@ -54,8 +58,8 @@ __device__ inline float load_shared(const float *p)
 
 // COHERENT: the partials come from other workgroups of the same launch (read with
 // load_shared); else from an earlier launch (plain loads).
-template <int kUnits, bool COHERENT = false>
-__device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const float *sinks,
+template <int kUnits, bool COHERENT, int kBatch>
+__device__ inline void merge_rows_b(const float *ws_o, const float *ws_lse, const float *sinks,
                                   uint16_t *out, float *lse, int b, int64_t c0, int n, int Hq,
                                   int nq, int Dv, int hq0, int nrows, int tid, int nthr)
 {
@@ -84,14 +88,14 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
             }
             acc[j] = merge_f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int i0 = 0; i0 < n; i0 += kChunkBatch) {
-            float lv[kUnits][kChunkBatch];
-            merge_f32x4 ov[kUnits][kChunkBatch];
+        for (int i0 = 0; i0 < n; i0 += kBatch) {
+            float lv[kUnits][kBatch];
+            merge_f32x4 ov[kUnits][kBatch];
 #pragma unroll
             for (int j = 0; j < kUnits; j++) {
                 const int d0 = ((u0 + j * nthr) % q4) * 4;
 #pragma unroll
-                for (int k = 0; k < kChunkBatch; k++) {
+                for (int k = 0; k < kBatch; k++) {
                     const bool in = ok[j] && i0 + k < n;
                     const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hr;
                     if (COHERENT) {
@@ -109,13 +113,13 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
             for (int j = 0; j < kUnits; j++) {
                 float mb = m[j];
 #pragma unroll
-                for (int k = 0; k < kChunkBatch; k++) mb = fmaxf(mb, lv[j][k]);
+                for (int k = 0; k < kBatch; k++) mb = fmaxf(mb, lv[j][k]);
                 if (mb == -INFINITY) continue;            // nothing non-empty yet
                 const float alpha = expf(m[j] - mb);      // m = -inf: 0
                 s[j] *= alpha;
                 acc[j] *= alpha;
 #pragma unroll
-                for (int k = 0; k < kChunkBatch; k++) {
+                for (int k = 0; k < kBatch; k++) {
                     if (lv[j][k] == -INFINITY) continue;  // empty chunk: no weight
                     const float w = expf(lv[j][k] - mb);
                     s[j] += w;
@@ -143,6 +147,18 @@ __device__ inline void merge_rows(const float *ws_o, const float *ws_lse, const 
             *(merge_bf16x4 *)(out + row * Dv + d0) = ob;
         }
     }
+}
+
+// merge_rows_b with the batch chosen at run time (merge_batch)
+template <int kUnits, bool COHERENT = false>
+__device__ inline void merge_rows(int batch, const float *ws_o, const float *ws_lse, const float *sinks,
+                                  uint16_t *out, float *lse, int b, int64_t c0, int n, int Hq,
+                                  int nq, int Dv, int hq0, int nrows, int tid, int nthr)
+{
+    if (batch == 4)
+        merge_rows_b<kUnits, COHERENT, 4>(ws_o, ws_lse, sinks, out, lse, b, c0, n, Hq, nq, Dv, hq0, nrows, tid, nthr);
+    else
+        merge_rows_b<kUnits, COHERENT, 8>(ws_o, ws_lse, sinks, out, lse, b, c0, n, Hq, nq, Dv, hq0, nrows, tid, nthr);
 }
 
 // Fused combine, called by every thread of a workgroup once it has processed all its
@@ -179,8 +195,8 @@ __device__ inline void fused_combine_tail(const DecodeArgs &a, const int32_t *pl
                       n * arrivals - 1;
         __syncthreads();
         if (*s_flag) {
-            merge_rows<kUnits, true>(a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0, n, Hq, nq, a.Dv, hq0,
-                                nrows, threadIdx.x, blockDim.x);
+            merge_rows<kUnits, true>(merge_batch(a.kv_format), a.ws_o, a.ws_lse, a.sinks, a.out, a.lse, b, c0,
+                                     n, Hq, nq, a.Dv, hq0, nrows, threadIdx.x, blockDim.x);
             if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
