@@ -110,7 +110,8 @@ typedef struct {
        pool + page * s_page + h * s_head + (t % page_size) * s_tok
        with page = block_table[b][t / page_size].  HND [page][Hkv][P][D]:
        s_page = Hkv*P*D, s_head = P*D, s_tok = D.  NHD [page][P][Hkv][D]:
-       s_page = P*Hkv*D, s_head = D, s_tok = Hkv*D.  MLA: s_tok = 656, s_head unused.
+       s_page = P*Hkv*D, s_head = D, s_tok = Hkv*D.  MLA: s_tok = 656 (656 .. 2^20
+       accepted, else PA_ERR_INVALID / PA_ERR_UNSUPPORTED), s_head unused.
        Every stride times the unit size must be a multiple of 16 bytes. */
     int64_t s_page, s_head, s_tok;
     int32_t q_len;             /* query tokens per request (a linear draft, token i sees keys

@@ -78,6 +78,7 @@ pa_status check_desc(const pa_decode_desc *d)
         if (d->G % 16 != 0 || d->G > 128) return PA_ERR_UNSUPPORTED;   // 16 heads per wave
         if (d->G * d->q_len > 1024) return PA_ERR_UNSUPPORTED;         // 16 groups of 64 rows
         if (d->s_tok < 656) return PA_ERR_INVALID;
+        if (d->s_tok > (1 << 20)) return PA_ERR_UNSUPPORTED;          // 32-bit token offsets
         return PA_OK;
     }
     if (d->D != d->Dv || (d->D != 64 && d->D != 128)) return PA_ERR_UNSUPPORTED;

@@ -192,6 +192,24 @@ __device__ __forceinline__ void lds_dma_buf16(const void *base, int nbytes, int 
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs) : "memory", "m0");
 }
+// a + b * c in 64 bits on the scalar unit, for uniform operands (b < 2^31).  The compiler
+// selects a vector multiply-add for 64-bit products even of uniform values; a vector
+// 64-bit multiply-add costs four times a plain vector instruction and its result then
+// needs moving back to scalar registers.
+__device__ __forceinline__ uint64_t s_mad64(uint64_t a, uint32_t b, uint64_t c)
+{
+    uint32_t lo, hi, t;
+    asm("s_mul_i32 %0, %3, %4\n\t"
+        "s_mul_hi_u32 %1, %3, %4\n\t"
+        "s_mul_i32 %2, %3, %5\n\t"
+        "s_add_i32 %1, %1, %2\n\t"
+        "s_add_u32 %0, %0, %6\n\t"
+        "s_addc_u32 %1, %1, %7"
+        : "=&s"(lo), "=&s"(hi), "=&s"(t)
+        : "s"(b), "s"((uint32_t)c), "s"((uint32_t)(c >> 32)), "s"((uint32_t)a), "s"((uint32_t)(a >> 32))
+        : "scc");
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ void lds_dma_glb4(const void *g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
@@ -211,14 +229,24 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
     return o;
 }
 
+// max(a, b) as one instruction: fmaxf quiets signalling NaN inputs first, which costs an
+// instruction per operand the compiler cannot prove canonical (values from LDS or from
+// lane permutes).  The operands here are logits or -inf, never NaN.
+__device__ __forceinline__ float max_nc(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // max / sum over the lanes l, l^16, l^32, l^48 (the 4 row groups of one MFMA column),
 // through the row-swap permutes (no LDS); the result is the same in all four lanes
 __device__ __forceinline__ float col_max(float x)
 {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = max_nc(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    return max_nc(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 __device__ __forceinline__ float col_sum(float x)
 {
@@ -364,9 +392,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 // ---- S^T of row block sb of tile t (rows: this lane's tokens 8g4 + 4sb + r) into
                 //      st[4]: per 128-dim scale tile u an fp32 partial of 4 bf16 MFMAs on the
                 //      converted codes, one partial for the rope dims (2 bf16 MFMAs), combined
-                //      with the token scales in fp32 as the tiles complete.  MFMA slot k: tile
-                //      k / 4, step k % 4 for k < 16, then rope 0, 1; the A operand of slot k + 1
-                //      is converted in slot k, codes are read about 6 slots before their use.
+                //      with the token scales in fp32 as the tiles complete.  MFMA slots 0, 1: rope;
+                //      slot k >= 2: tile (k - 2) / 4, step (k - 2) % 4; the A operand of a slot is
+                //      converted in the slot before, codes are read 3 slots before that.
                 //      step(k) runs in slot k, before its MFMA: the VALU work of the previous
                 //      tile, issued while the matrix core works.
                 auto qk_tile = [&](int t, float (&st)[4], auto &&step) {
@@ -393,33 +421,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         for (int r = 0; r < 4; r++)
                             scu[u & 1][r] = *(PA_LDS const float *)(slot + sc_off + r * kRowStep + 4 * u);
                     };
+                    kr[0] = *(PA_LDS const bf16x8 *)(slot + rope_off);
+                    kr[1] = *(PA_LDS const bf16x8 *)(slot + rope_off + 64);
                     kc[0] = rd_codes(0);
                     bf16x8 av[2];
-                    av[0] = cvt(kc[0], 0);
 #pragma unroll
                     for (int k = 0; k < 18; k++) {
-                        // reads issued at this slot: the next tile's codes 4 slots before their
-                        // first use, the scales of tile u after its MFMAs start, rope at slot 10
-                        if (k < 16 && (k & 3) == 0 && k + 4 < 16) kc[((k >> 2) + 1) & 1] = rd_codes((k >> 2) + 1);
-                        if (k < 16 && (k & 3) == 1) rd_scales(k >> 2);
-                        if (k == 10) {
-                            kr[0] = *(PA_LDS const bf16x8 *)(slot + rope_off);
-                            kr[1] = *(PA_LDS const bf16x8 *)(slot + rope_off + 64);
-                        }
+                        const int j = k - 2;           // latent step of slot k >= 2
+                        // reads issued at this slot: the next tile's codes 3 slots before their
+                        // conversion, the scales of tile u after its MFMAs start
+                        if (j >= 0 && (j & 3) == 0 && j + 4 < 16) kc[((j >> 2) + 1) & 1] = rd_codes((j >> 2) + 1);
+                        if (j >= 0 && (j & 3) == 1) rd_scales(j >> 2);
                         step(k);
-                        if (k < 16) {
-                            part[k >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k & 1], qb[k >> 2][k & 3], part[k >> 2], 0, 0, 0);
+                        if (k < 2) {
+                            part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qrope[k], part[4], 0, 0, 0);
                         } else {
-                            part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k - 16], qrope[k - 16], part[4], 0, 0, 0);
+                            part[j >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j & 1], qb[j >> 2][j & 3], part[j >> 2], 0, 0, 0);
                         }
-                        if (k + 1 < 16) av[(k + 1) & 1] = cvt(kc[((k + 1) >> 2) & 1], (k + 1) & 3);
+                        if (k >= 1 && j + 1 < 16) av[(j + 1) & 1] = cvt(kc[((j + 1) >> 2) & 1], (j + 1) & 3);
                         // the token scales times the tile partials, three slots after a tile's
-                        // last MFMA (tile 3's and the rope partial after the loop)
-                        if (k == 6 || k == 10 || k == 14) {
-                            const int u = (k - 6) >> 2;
+                        // last MFMA (tile 3's after the loop); the rope partial starts the sum
+                        if (k == 8 || k == 12 || k == 16) {
+                            const int u = (k - 8) >> 2;
 #pragma unroll
                             for (int r = 0; r < 4; r++) {
-                                float y = u == 0 ? 0.f : x[r];
+                                float y = u == 0 ? part[4][r] : x[r];
                                 y += scu[u & 1][r] * part[u][r];
                                 asm volatile("" : "+v"(y));    // computed in this slot
                                 x[r] = y;
@@ -428,7 +454,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         __builtin_amdgcn_sched_barrier(0);
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; r++) st[r] = x[r] + scu[1][r] * part[3][r] + part[4][r];
+                    for (int r = 0; r < 4; r++) st[r] = x[r] + scu[1][r] * part[3][r];
                 };
 
                 // ---- logits of row block sb of tile t (log2 domain, masked) and their max per
@@ -444,10 +470,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         const int tok = t0 + kT * t + 8 * g4 + 4 * sb + r;
                         const bool vis = SPARSE ? ((vmask >> r) & 1u) != 0
                                                 : MASKED ? (tok < tlim && tok >= tlo) : tok < t1;
-                        sv[r] = vis ? st[r] * a.scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, sv[r]);
+                        sv[r] = vis ? st[r] : -INFINITY;    // unscaled; the scale c > 0 joins in
+                        mx = fmaxf(mx, sv[r]);                //   the max and the exponent
                     }
-                    bm_own = col_max(mx);
+                    bm_own = col_max(mx) * a.scale_log2;
                     if (g4 == 0) s_tmax[t & 1][sb][hg][col] = bm_own;
                 };
 
@@ -473,7 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     auto softmax_step = [&](int s) {
                         if (s == 0) bm_other = s_tmax[i & 1][sb ^ 1][hg][col];
                         if (s == 2) {
-                            const float bm = fmaxf(bm_own, bm_other);
+                            const float bm = max_nc(bm_own, bm_other);
                             m_new = bm > m + kLazyMax ? bm : m;
                             alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
                             mref = m_new == -INFINITY ? 0.f : m_new;
@@ -481,7 +507,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         if (s == 3 || s == 4) {
 #pragma unroll
                             for (int r = 2 * (s - 3); r < 2 * (s - 3) + 2; r++) {
-                                pr[r] = fast_exp2(sv[r] - mref);
+                                pr[r] = fast_exp2(fmaf(sv[r], a.scale_log2, -mref));
                                 ps += pr[r];
                             }
                         }
@@ -619,14 +645,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             //      issue a tile's 8 token loads one per 16-dim block of their PV MFMAs: a
             //      burst of all of them at the loop top stalls the issue for hundreds of cycles.
             struct TileLoads {
-                const uint8_t *tok;                // dense: the first token's bytes
-                int nreal;                         // dense: real tokens of the 8
+                const uint8_t *tok;                // dense: the first token's bytes (uniform)
+                int nreal;                         // dense: real tokens of the 8; sparse: their bits
                 int pos, pgv;                      // sparse: lane l: token l's position, page id
                 uint32_t lds0;                     // LDS row of the first token
             };
             auto prep_tile = [&](int t, int page) {
                 TileLoads L;
-                L.lds0 = lds_addr(&raw[t % kRawSlots][raw_row(kTokPerWave * lw)]);
+                L.lds0 = (uint32_t)uniform((int)lds_addr(&raw[t % kRawSlots][raw_row(kTokPerWave * lw)]));
                 L.tok = nullptr;
                 L.nreal = 0;
                 L.pos = L.pgv = 0;
@@ -646,10 +672,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     L.nreal = (int)vm;             // sparse: the real-token bits
                     if (lane == 0) s_valid[t % kRawSlots][lw] = (uint8_t)vm;
                 } else {
-                    // the 8 tokens are consecutive slots of one page
-                    const int tw = t0 + kT * t + kTokPerWave * lw;     // first of the 8 tokens
-                    L.tok = a.k_pool + (int64_t)page * a.s_page_b + (int64_t)(tw & page_mask) * a.s_tok_b;
-                    L.nreal = min(max(t1 - tw, 0), kTokPerWave);
+                    // the 8 tokens are consecutive slots of one page; addresses on the scalar
+                    // unit (the token stride is below 2^20 bytes)
+                    const int tw = uniform(t0 + kT * t + kTokPerWave * lw);   // first of the 8 tokens
+                    const uint64_t pg = s_mad64((uint64_t)(uintptr_t)a.k_pool, (uint32_t)page, (uint64_t)a.s_page_b);
+                    L.tok = (const uint8_t *)(uintptr_t)(pg + (uint32_t)(tw & page_mask) * (uint32_t)a.s_tok_b);
+                    L.nreal = uniform(min(max(t1 - tw, 0), kTokPerWave));
                 }
                 return L;
             };
@@ -663,8 +691,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     const uint8_t *src = a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0);
                     if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
                 } else {
+                    // (a buffer per token: the range check of a buffer load leaves out the
+                    // scalar offset, so a token past the real ones needs a buffer of its own)
                     if (lane < kChunks)
-                        lds_dma_buf16(L.tok + (int64_t)tt * a.s_tok_b, tt < L.nreal ? kTokBytes : 0, 16 * lane,
+                        lds_dma_buf16(L.tok + tt * (uint32_t)a.s_tok_b, tt < L.nreal ? kTokBytes : 0, 16 * lane,
                                       L.lds0 + tok_row(tt));
                 }
             };

@@ -299,6 +299,30 @@ def test_mla_q_dynamic_range():
     assert_parity(case, out, lse, ref_out, ref_lse)
 
 
+@pytest.mark.parametrize("kw", [dict(lens=(300, 33, 1000, 7)), dict(lens=(129, 70), G=32, P=16, splits=3)])
+def test_mla_tail_slots_poisoned(kw):
+    """Every token slot past a request's length in its last page, and every unused page,
+    holds 0xFF bytes (NaN codes, scales and rope values).  The kernel loads a tile's
+    tokens past the item as zeros and masks their logits; none of those bytes may reach
+    the result."""
+    case = _mla_case(**kw)
+    P = case["page_size"]
+    used = set()
+    for b, L in enumerate(case["seq_lens"]):
+        for j in range(-(-L // P)):
+            pg = case["block_table"][b, j]
+            used.add(int(pg))
+            lo = L - j * P
+            if lo < P:
+                case["k_pool"][pg, lo:] = 0xFF
+    for pg in range(case["k_pool"].shape[0]):
+        if pg not in used:
+            case["k_pool"][pg] = 0xFF
+    out, lse = DecodeRun(case)()
+    ref_out, ref_lse = oracle.decode(case)
+    assert_parity(case, out, lse, ref_out, ref_lse)
+
+
 @pytest.mark.parametrize("splits", [0, 1])
 def test_mla_needle(splits):
     lens = (257, 96)
