@@ -647,7 +647,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             struct TileLoads {
                 const uint8_t *tok;                // dense: the first token's bytes (uniform)
                 int nreal;                         // dense: real tokens of the 8; sparse: their bits
-                int pos, pgv;                      // sparse: lane l: token l's position, page id
+                uint32_t off_lo, off_hi;           // sparse: lane l: byte offset of token l % 8 in the pool
                 uint32_t lds0;                     // LDS row of the first token
             };
             auto prep_tile = [&](int t, int page) {
@@ -655,20 +655,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 L.lds0 = (uint32_t)uniform((int)lds_addr(&raw[t % kRawSlots][raw_row(kTokPerWave * lw)]));
                 L.tok = nullptr;
                 L.nreal = 0;
-                L.pos = L.pgv = 0;
+                L.off_lo = L.off_hi = 0;
                 if (SPARSE) {
                     const int pos_look = sp_read(0, t + kAhead);
                     sp_issue_page(t + kAhead, pos_look);
                     sp_issue_pos(t + 2 * kAhead);
-                    L.pos = sp_read(0, t);
-                    L.pgv = sp_read(1, t);
-                    uint32_t vm = 0;
-#pragma unroll
-                    for (int tt = 0; tt < kTokPerWave; tt++) {
-                        const int p = __builtin_amdgcn_readlane(L.pos, tt);
-                        const int k = t0 + kT * t + kTokPerWave * lw + tt;
-                        vm |= (k < t1 && p >= 0 && p < Lb ? 1u : 0u) << tt;
-                    }
+                    // lane l works out token l % 8 of the wave's 8 (all 8 at once on the vector
+                    // unit; per token on the scalar unit this took ~40 instructions)
+                    const int pos = sp_read(0, t);
+                    const int pgv = sp_read(1, t);
+                    const int k = t0 + kT * t + kTokPerWave * lw + (lane & (kTokPerWave - 1));
+                    const bool vis = k < t1 && pos >= 0 && pos < Lb;
+                    const uint64_t off = vis ? (uint64_t)(uint32_t)pgv * (uint64_t)a.s_page_b +
+                                                   (uint64_t)((uint32_t)(pos & page_mask) * (uint32_t)a.s_tok_b)
+                                             : 0;
+                    L.off_lo = (uint32_t)off;
+                    L.off_hi = (uint32_t)(off >> 32);
+                    const uint32_t vm = (uint32_t)__ballot(vis) & ((1u << kTokPerWave) - 1);
                     L.nreal = (int)vm;             // sparse: the real-token bits
                     if (lane == 0) s_valid[t % kRawSlots][lw] = (uint8_t)vm;
                 } else {
@@ -685,11 +688,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             auto tok_row = [](int tt) { return (tt >> 2) * kHalfGroupBytes + (tt & 3) * kRowStep; };
             auto dma_token = [&](const TileLoads &L, int tt) {
                 if (SPARSE) {
-                    const int p = __builtin_amdgcn_readlane(L.pos, tt);
-                    const int pg = __builtin_amdgcn_readlane(L.pgv, tt);
+                    const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)L.off_hi, tt) << 32) |
+                                         (uint32_t)__builtin_amdgcn_readlane((int)L.off_lo, tt);
                     const bool ok = (L.nreal >> tt) & 1;
-                    const uint8_t *src = a.k_pool + (ok ? (int64_t)pg * a.s_page_b + (int64_t)(p & page_mask) * a.s_tok_b : 0);
-                    if (lane < kChunks) lds_dma_buf16(src, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
+                    if (lane < kChunks) lds_dma_buf16(a.k_pool + off, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
                 } else {
                     // (a buffer per token: the range check of a buffer load leaves out the
                     // scalar offset, so a token past the real ones needs a buffer of its own)
