@@ -42,9 +42,10 @@
 //     iteration i (tiles i and i+1 are waited for at its top: the score waves read tile
 //     i+1's keys).  Page ids come the same way, 3 tiles ahead, into a small LDS ring (a
 //     scalar load would make every later LDS wait also wait for it);
-//   * scores: per 128-dim scale tile u, four bf16 MFMAs 16x16x32 on the codes converted
-//     in registers; rope dims: two bf16 MFMAs; S = sum_u scale_t,u (q_u . code_t,u) +
-//     q_rope . k_rope in fp32;
+//   * scores: rope dims: two bf16 MFMAs 16x16x32 (first, so that their partial starts the
+//     sum); per 128-dim scale tile u, four on the codes converted in registers;
+//     S = q_rope . k_rope + sum_u scale_t,u (q_u . code_t,u) in fp32; the logit scale c > 0
+//     joins in the maximum and in the exponent, p = 2^(c S - m);
 //   * an online softmax per head column (the previous tile's, in the MFMA slots of the next
 //     tile's scores); the score waves write P^T times each 128-dim value tile's token
 //     scales (bf16, the B operands of the PV MFMAs; each wave its half of the tokens) and
@@ -62,17 +63,18 @@
 // the 128-dim tile (one per k-step), the same for K and Q.
 // One workgroup barrier per tile: it publishes the PV operands and half-tile maxima, and
 // frees the ring slot of tile i-2.  The running max is only moved when a tile's max
-// exceeds it by more than 2^8, so the rescale of O^T is rare; probabilities stay below 2^8
-// and the result is the same up to rounding (the reference cancels in the final
+// exceeds it by more than 8 (log2 units), so the rescale of O^T is rare; probabilities stay
+// below 2^8 and the result is the same up to rounding (the reference cancels in the final
 // normalisation).
 //
 // Sparse decode (FlashMLA walk-through, section 调度: the decode call takes sparse
 // indices): the items then cover index slots, and slot k of request b names the key
 // position indices[b][k].  The address of a listed token takes two dependent lookups
-// (index, then block table); lanes 0-3 of each score wave (its 4 tokens of a tile) load
+// (index, then block table); lanes 0-7 of each value wave (its 8 tokens of a tile) load
 // them direct to LDS, positions 6 tiles and page ids 3 tiles ahead of the tile's own
-// loads, so that every wait for them is one the KV ring does anyway.  A slot outside the
-// item or the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
+// loads, so that every wait for them is one the KV ring does anyway; the 8 token addresses
+// are then worked out on the vector unit, one lane per token.  A slot outside the item or
+// the request loads nothing (zeros), and a per-tile bit mask of the real tokens is
 // applied in the softmax.
 #include "pa_internal.h"
 #include "pa_merge.h"
