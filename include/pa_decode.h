@@ -38,9 +38,10 @@
  * each other; on MI355X the merging workgroup then waits for those stores, the counter
  * and the coherent reads in turn, which on small workloads costs more than the combine
  * launch it saves.
- * Ordering: the writers use relaxed agent-scope atomic stores, wait for their completion
- * (s_waitcnt vmcnt(0)) and then bump the counter with a relaxed agent-scope atomic; the
- * merger reads with relaxed agent-scope atomic loads.  This is not release/acquire in
+ * Ordering: the writers store their partials with the cache policy of relaxed agent-scope
+ * atomics (sc1, 16 bytes per access), wait for their completion (s_waitcnt vmcnt(0)) and
+ * then bump the counter with a relaxed agent-scope atomic; the merger reads with the same
+ * policy.  This is not release/acquire in
  * the HIP memory model: it relies on gfx950 executing agent-scope atomics on memory that
  * is coherent across XCDs (the write-through policy those accesses carry), so a store
  * that has completed is visible to every later agent-scope load.  An agent-scope

@@ -460,8 +460,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                     const int64_t prow = (int64_t)it * nq * Hq + qr;
                     float *dst = a.ws_o + prow * a.Dv + d0;
                     if (a.counters) {                 // merged inside this launch
-#pragma unroll
-                        for (int k = 0; k < 8; k++) store_shared(dst + k, o[k]);
+                        // (a buffer over the item's partial rows; `it` is uniform)
+                        const int64_t prow0 = (int64_t)it * nq * Hq;
+                        const __amdgpu_buffer_rsrc_t rows = shared_rows(a.ws_o + prow0 * a.Dv, (int64_t)nq * Hq * a.Dv * 4);
+                        const uint32_t off = (uint32_t)(((prow - prow0) * a.Dv + d0) * 4);
+                        store_shared4(rows, off, merge_f32x4{o[0], o[1], o[2], o[3]});
+                        store_shared4(rows, off + 16, merge_f32x4{o[4], o[5], o[6], o[7]});
                         if (d0 == 0) store_shared(a.ws_lse + prow, lse_v);
                     } else {
                         *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};

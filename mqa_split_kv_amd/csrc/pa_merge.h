@@ -43,7 +43,8 @@ typedef float merge_f32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ inline int merge_batch(int kv_format) { return kv_format == PA_KV_MLA656 ? 4 : 8; }
 
 // Partials shared across workgroups inside one launch (the fused combine) are written and
-// read with agent-scope relaxed atomics: on gfx950 such stores and loads are coherent at
+// read with the cache policy of agent-scope relaxed atomics: on gfx950 such stores and
+// loads (single floats here, 16 bytes through the buffer helpers below) are coherent at
 // device scope by themselves (the sc1 cache policy: through the non-coherent per-XCD L2),
 // so ordering them only takes a wait for the stores and the counter atomic, and no fence,
 // i.e. no write-back or invalidation of the whole L2.
@@ -54,6 +55,22 @@ __device__ inline void store_shared(float *p, float v)
 __device__ inline float load_shared(const float *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same cache policy (sc1) on 16-byte accesses, through a buffer over a uniform range of
+// partial rows (one item's or one request's, far below 2^32 bytes): a quarter of the
+// memory instructions of four single-float accesses.  `base` must be uniform.
+__device__ inline __amdgpu_buffer_rsrc_t shared_rows(const float *base, int64_t nbytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)nbytes, 0x00020000);
+}
+constexpr int kCoherentPolicy = 16;     // the sc1 bit of the buffer instructions' cache policy
+__device__ inline merge_f32x4 load_shared4(__amdgpu_buffer_rsrc_t rows, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(rows, byte_off, 0, kCoherentPolicy);
+}
+__device__ inline void store_shared4(__amdgpu_buffer_rsrc_t rows, uint32_t byte_off, merge_f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, rows, byte_off, 0, kCoherentPolicy);
 }
 
 // COHERENT: the partials come from other workgroups of the same launch (read with
@@ -66,6 +83,8 @@ __device__ inline void merge_rows_b(const float *ws_o, const float *ws_lse, cons
     const int q4 = Dv / 4;
     const int total = nq * nrows * q4;
     const int64_t Hr = (int64_t)nq * Hq;                 // query rows per request / chunk
+    // COHERENT: the request's n chunks of partial rows, read 16 bytes at a time
+    const __amdgpu_buffer_rsrc_t rows_o = shared_rows(ws_o + c0 * Hr * Dv, COHERENT ? (int64_t)n * Hr * Dv * 4 : 0);
     auto qrow = [&](int u) {
         const int rr = u / q4;
         return (rr / nrows) * Hq + hq0 + rr % nrows;
@@ -100,8 +119,8 @@ __device__ inline void merge_rows_b(const float *ws_o, const float *ws_lse, cons
                     const int64_t prow = prow0[j] + (int64_t)(i0 + k) * Hr;
                     if (COHERENT) {
                         lv[j][k] = in ? load_shared(ws_lse + prow) : -INFINITY;
-#pragma unroll
-                        for (int e = 0; e < 4; e++) ov[j][k][e] = in ? load_shared(ws_o + prow * Dv + d0 + e) : 0.f;
+                        ov[j][k] = in ? load_shared4(rows_o, (uint32_t)(((prow - c0 * Hr) * Dv + d0) * 4))
+                                      : merge_f32x4{0.f, 0.f, 0.f, 0.f};
                     } else {
                         lv[j][k] = in ? ws_lse[prow] : -INFINITY;
                         ov[j][k] = in ? *(const merge_f32x4 *)(ws_o + prow * Dv + d0)
@@ -164,10 +183,10 @@ __device__ inline void merge_rows(int batch, const float *ws_o, const float *ws_
 // Fused combine, called by every thread of a workgroup once it has processed all its
 // items [ib, ie) (kUnits: the merge's units per thread and pass, as in merge_rows) (row group rg: query heads [hq0, hq0 + nrows) of every query token;
 // `arrivals` workgroups write partials per chunk of the row group).  The partials were
-// written with store_shared; each thread waits until its stores are complete, the
+// written with store_shared / store_shared4; each thread waits until its stores are complete, the
 // workgroup meets, and one thread counts each of the workgroup's partial chunks in with a
 // device-scope atomic; the workgroup that counts a request's last chunk reads the other
-// workgroups' partials with load_shared (every store it needs completed before the count
+// workgroups' partials with load_shared / load_shared4 (every store it needs completed before the count
 // it observed), merges that request, and returns its counter to zero.  Then requests with no chunk at all (length 0 under the
 // balanced rule) get out = 0, lse = -inf (or the sink) from workgroup part = b mod
 // num_parts.

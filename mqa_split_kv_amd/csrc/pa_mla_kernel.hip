@@ -858,11 +858,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     } else {
                         float *orow = a.ws_o + ((int64_t)it * nq * Hq + row) * kDv + 128 * vt + 4 * g4;
                         if (!SPARSE && a.counters) {         // merged inside this launch
+                            // (a buffer over the item's partial rows; `it` is uniform)
+                            const __amdgpu_buffer_rsrc_t rows =
+                                shared_rows(a.ws_o + (int64_t)it * nq * Hq * kDv, (int64_t)nq * Hq * kDv * 4);
+                            const uint32_t off = (uint32_t)((row * kDv + 128 * vt + 4 * g4) * 4);
 #pragma unroll
-                            for (int d = 0; d < kVBlocks; d++) {
-#pragma unroll
-                                for (int e = 0; e < 4; e++) store_shared(orow + 16 * d + e, acc[4 * d + hb][e] * inv);
-                            }
+                            for (int d = 0; d < kVBlocks; d++) store_shared4(rows, off + 64 * d, acc[4 * d + hb] * inv);
                         } else {
 #pragma unroll
                             for (int d = 0; d < kVBlocks; d++) *(f32x4 *)(orow + 16 * d) = acc[4 * d + hb] * inv;
@@ -873,10 +874,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         }
     }
     // fused combine (dense, one query token: the head group is heads [64 group, 64 group +
-    // 64)): the last workgroup to finish a request's chunks merges them, one unit per
-    // thread and pass (768 threads; more units would need more registers than the waves have)
+    // 64)): the last workgroup to finish a request's chunks merges them, two units per
+    // thread and pass (768 threads; four spill registers in the main loops)
     if (!SPARSE && a.counters)
-        fused_combine_tail<1>(a, plan, part, ib, ie, group, ngroups, group * kHeadsPerWG,
+        fused_combine_tail<2>(a, plan, part, ib, ie, group, ngroups, group * kHeadsPerWG,
                            min(kHeadsPerWG, G - group * kHeadsPerWG), 1, &s_flag);
 }
 
