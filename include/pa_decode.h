@@ -29,7 +29,9 @@
  *   pa_decode_combine  LSE-weighted merge of the partials into out / lse
  *
  * With PA_FLAG_FUSED_COMBINE (bf16 and fp8 page-head formats; MLA-656 with q_len 1 and
- * no sparse indices) the merge runs inside pa_decode_run instead: the workgroup that
+ * no sparse indices; the partial rows of one request, chunks x q_len x Hkv x G x Dv x 4
+ * bytes with up to num_splits chunks, or 1024 under the balanced plan, below 2 GiB, else
+ * PA_ERR_UNSUPPORTED) the merge runs inside pa_decode_run instead: the workgroup that
  * finishes the last chunk of a request merges that request's chunks (the XQA article's
  * "last CTA merges" variant, section "归约怎么记"), found with a device-scope counter per
  * (request, row group) kept in the plan buffer; then pa_decode_combine has nothing to do

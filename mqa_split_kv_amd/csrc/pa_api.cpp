@@ -67,6 +67,13 @@ pa_status check_desc(const pa_decode_desc *d)
     if (P != 16 && P != 32 && P != 64 && P != 128 && P != 256) return PA_ERR_UNSUPPORTED;
     if (d->B > pa::kMaxBatch) return PA_ERR_UNSUPPORTED;
     if (d->num_splits > 256) return PA_ERR_UNSUPPORTED;
+    // fused combine: the merging workgroup reaches a request's partial rows through one
+    // buffer with 32-bit byte offsets; a request has at most num_splits chunks (balanced
+    // plan: at most kMaxPlanParts)
+    if ((d->flags & PA_FLAG_FUSED_COMBINE) &&
+        (int64_t)(d->num_splits > 0 ? d->num_splits : pa::kMaxPlanParts) * d->q_len * d->Hkv * d->G * d->Dv * 4 >=
+            ((int64_t)1 << 31))
+        return PA_ERR_UNSUPPORTED;
     if ((int64_t)d->max_pages_per_seq * P > (int64_t)1 << 30) return PA_ERR_UNSUPPORTED;
     if (d->kv_format == PA_KV_MLA656) {
         // fused combine: one query token (a head group of the MLA kernel is then a range

@@ -71,6 +71,7 @@ BAD = [
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=128, D=576, Dv=512, s_tok=656, s_page=656 * 16,
           q_len=9), pb.PA_ERR_UNSUPPORTED),     # more than 1024 query rows
     (dict(B=5000), pb.PA_ERR_UNSUPPORTED),
+    (dict(Hkv=512, G=16, q_len=16, num_splits=0, flags=1), pb.PA_ERR_UNSUPPORTED),  # fused: partials >= 2 GiB
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=1, G=16, D=576, Dv=512, s_tok=(1 << 20) + 16,
           s_page=((1 << 20) + 16) * 16), pb.PA_ERR_UNSUPPORTED),   # MLA token stride over 2^20 B
     (dict(kv_format=pb.PA_KV_MLA656, Hkv=2, D=576, Dv=512, s_tok=656, s_page=656 * 16),
