@@ -79,6 +79,8 @@
 #include "pa_internal.h"
 #include "pa_merge.h"
 
+#include <utility>
+
 namespace pa {
 namespace {
 
@@ -128,6 +130,18 @@ static_assert(kTokPerWave == 128 / 16, "a value wave issues one token load per 1
 static_assert(kLookRing > 2 * kAhead && (kLookRing & (kLookRing - 1)) == 0, "lookup ring");
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}) in order
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 // LDS byte offset of token row r (0..31) in a tile slot.  LDS has 64 four-byte banks; a
 // 16-byte read serves 16 lanes per cycle, lanes {0-3, 12-15, 20-23, 24-27} together and
@@ -399,8 +413,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 //      converted in the slot before, codes are read 3 slots before that.
                 //      step(k) runs in slot k, before its MFMA: the VALU work of the previous
                 //      tile, issued while the matrix core works.
-                auto qk_tile = [&](int t, float (&st)[4], auto &&step) {
-                    PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t % kRawSlots];
+                auto qk_tile = [&](int t_slot, float (&st)[4], auto &&step) {
+                    PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t_slot];
                     auto rd_codes = [&](int u) {
                         PA_LDS const uint8_t *p = slot + qk_off + 128 * u;
                         const u32x4 x = *(PA_LDS const u32x4 *)p;
@@ -462,10 +476,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 // ---- logits of row block sb of tile t (log2 domain, masked) and their max per
                 //      head, published for the other half of the tile
                 float sv[4], bm_own = -INFINITY;
-                auto finish_tile = [&](int t, const float (&st)[4]) {
+                auto finish_tile = [&](int t, int t_slot, int t_par, const float (&st)[4]) {
                     uint32_t vmask = 0;
                     if (SPARSE)                        // tokens 8g4 + 4sb + r: loader g4, bits 4sb + r
-                        vmask = (uint32_t)s_valid[t % kRawSlots][g4] >> (4 * sb);
+                        vmask = (uint32_t)s_valid[t_slot][g4] >> (4 * sb);
                     float mx = -INFINITY;
                     if (!SPARSE && !MASKED && t0 + kT * (t + 1) <= t1) {
                         // a tile wholly inside the item (all but the last): no mask (a uniform
@@ -486,19 +500,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         }
                     }
                     bm_own = col_max(mx) * a.scale_log2;
-                    if (g4 == 0) s_tmax[t & 1][sb][hg][col] = bm_own;
+                    if (g4 == 0) s_tmax[t_par][sb][hg][col] = bm_own;
                 };
 
                 {
                     float st0[4];
                     if (ntiles > 0) {
                         qk_tile(0, st0, [](int) {});
-                        finish_tile(0, st0);
+                        finish_tile(0, 0, 0, st0);
                     }
                 }
-                for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
-                    tile_top(i);                   // tiles i and i + 1 are in LDS, tile i's maxima out
-                    if (i == ntiles) break;
+                // one iteration: softmax of tile i, S^T of tile i + 1.  The ring slots and the
+                // parity are compile-time constants of the unrolled loop below (LDS offsets
+                // become immediates instead of a vector add per address and tile).
+                auto iteration = [&](int i, auto SLOT_I, auto SLOT_N, auto PAR) {
+                    constexpr int slot_i = decltype(SLOT_I)::value, slot_n = decltype(SLOT_N)::value;
+                    constexpr int par = decltype(PAR)::value;
                     // ---- softmax of tile i, spread over the MFMA slots of tile i + 1's S^T: the
                     //      tile's max (both halves), the lazily moved reference, p = 2^(s - m) and
                     //      this lane's row sum; P and the factor for O^T (1 unless the reference
@@ -509,7 +526,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     f32x4 scr[2];                      // tile i's token scales, read again
                     bf16x4 pb[4];
                     auto softmax_step = [&](int s) {
-                        if (s == 0) bm_other = s_tmax[i & 1][sb ^ 1][hg][col];
+                        if (s == 0) bm_other = s_tmax[par][sb ^ 1][hg][col];
                         if (s == 2) {
                             const float bm = max_nc(bm_own, bm_other);
                             m_new = bm > m + kLazyMax ? bm : m;
@@ -532,7 +549,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         // scales), from the scale rows read again one step before their use (row
                         // q read in step 5 + q into scr[q & 1], used in step 6 + q)
                         if (s >= 5 && s < 9)
-                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[i % kRawSlots] + sc_off + (s - 5) * kRowStep);
+                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[slot_i] + sc_off + (s - 5) * kRowStep);
                         if (s >= 6 && s < 10) {
                             const int r = s - 6;
 #pragma unroll
@@ -541,17 +558,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         if (s == 11 || s == 12) {
 #pragma unroll
                             for (int t = 2 * (s - 11); t < 2 * (s - 11) + 2; t++)
-                                s_p[i & 1][hg][t][sb][lane] = pb[t];
+                                s_p[par][hg][t][sb][lane] = pb[t];
                         }
                         if (s == 13) {
                             // both halves hold the same factor and both write it (no branch in the
                             // body, which would let the compiler sink the MFMAs past it)
-                            s_alpha[i & 1][hg][col] = alpha;
+                            s_alpha[par][hg][col] = alpha;
                         }
                     };
                     float st_nxt[4];
-                    qk_tile(i + 1, st_nxt, softmax_step);
-                    finish_tile(i + 1, st_nxt);
+                    qk_tile(slot_n, st_nxt, softmax_step);
+                    finish_tile(i + 1, slot_n, par ^ 1, st_nxt);
+                };
+                // iterations i = 0 .. ntiles (the last only meets the barrier), unrolled by 10
+                // (the ring's 5 slots x the 2 parities)
+                static_assert(10 % kRawSlots == 0, "the unrolled loop cycles through the ring's slots");
+                bool done = ntiles <= 0;
+                for (int i0 = 0; !done; i0 += 10) {
+                    static_for<10>([&](auto U) {
+                        constexpr int u = decltype(U)::value;
+                        if (done) return;
+                        const int i = i0 + u;
+                        tile_top(i);           // tiles i and i + 1 are in LDS, tile i's maxima out
+                        if (i == ntiles) {
+                            done = true;
+                            return;
+                        }
+                        iteration(i, std::integral_constant<int, u % kRawSlots>{},
+                                  std::integral_constant<int, (u + 1) % kRawSlots>{}, std::integral_constant<int, u & 1>{});
+                    });
                 }
 
                 // ---- epilogue: the row sum of both halves, 1 / l (with a sink of a whole-request
