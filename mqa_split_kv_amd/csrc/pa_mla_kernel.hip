@@ -694,7 +694,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             struct TileLoads {
                 const uint8_t *tok;                // dense: the first token's bytes (uniform)
                 int nreal;                         // dense: real tokens of the 8; sparse: their bits
-                uint32_t off_lo, off_hi;           // sparse: lane l: byte offset of token l % 8 in the pool
+                uint64_t toff[kTokPerWave];        // sparse: byte offsets of the 8 tokens in the pool (uniform)
                 uint32_t lds0;                     // LDS row of the first token
             };
             auto prep_tile = [&](int t, int page) {
@@ -702,7 +702,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 L.lds0 = (uint32_t)uniform((int)lds_addr(&raw[t % kRawSlots][raw_row(kTokPerWave * lw)]));
                 L.tok = nullptr;
                 L.nreal = 0;
-                L.off_lo = L.off_hi = 0;
+#pragma unroll
+                for (int tt = 0; tt < kTokPerWave; tt++) L.toff[tt] = 0;
                 if (SPARSE) {
                     const int pos_look = sp_read(0, t + kAhead);
                     sp_issue_page(t + kAhead, pos_look);
@@ -716,8 +717,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     const uint64_t off = vis ? (uint64_t)(uint32_t)pgv * (uint64_t)a.s_page_b +
                                                    (uint64_t)((uint32_t)(pos & page_mask) * (uint32_t)a.s_tok_b)
                                              : 0;
-                    L.off_lo = (uint32_t)off;
-                    L.off_hi = (uint32_t)(off >> 32);
+#pragma unroll
+                    for (int tt = 0; tt < kTokPerWave; tt++)
+                        L.toff[tt] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(off >> 32), tt) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)off, tt);
                     const uint32_t vm = (uint32_t)__ballot(vis) & ((1u << kTokPerWave) - 1);
                     L.nreal = (int)vm;             // sparse: the real-token bits
                     if (lane == 0) s_valid[t % kRawSlots][lw] = (uint8_t)vm;
@@ -735,10 +738,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             auto tok_row = [](int tt) { return (tt >> 2) * kHalfGroupBytes + (tt & 3) * kRowStep; };
             auto dma_token = [&](const TileLoads &L, int tt) {
                 if (SPARSE) {
-                    const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)L.off_hi, tt) << 32) |
-                                         (uint32_t)__builtin_amdgcn_readlane((int)L.off_lo, tt);
                     const bool ok = (L.nreal >> tt) & 1;
-                    if (lane < kChunks) lds_dma_buf16(a.k_pool + off, ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
+                    if (lane < kChunks) lds_dma_buf16(a.k_pool + L.toff[tt], ok ? kTokBytes : 0, 16 * lane, L.lds0 + tok_row(tt));
                 } else {
                     // (a buffer per token: the range check of a buffer load leaves out the
                     // scalar offset, so a token past the real ones needs a buffer of its own)
@@ -818,9 +819,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 i32x2 vw[3];
                 for (int i = 0; ntiles > 0 && i <= ntiles; i++) {
                     const TileLoads ld = tile_top(i);
-                    // (sparse: the token addresses take two lookups each; spread over the MFMAs
-                    // they would need more registers than the wave has, so they go out here)
-                    if (i == 0 || SPARSE) {
+                    if (i == 0) {
 #pragma unroll
                         for (int tt = 0; tt < kTokPerWave; tt++) dma_token(ld, tt);
                     }
@@ -858,7 +857,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         for (int d = 0; d < kVBlocks; d++) {
 #pragma unroll
                             for (int hb = 0; hb < 4; hb++) mfma_acc(acc[4 * d + hb], va[d & 1], pbt[hb]);
-                            if (!SPARSE) dma_token(ld, d); // token d of tile i + kAhead
+                            dma_token(ld, d);              // token d of tile i + kAhead
                             if (d + 3 < kVBlocks) vw[d % 3] = rd(vb, d + 3);
                             if (d + 1 < kVBlocks) {
                                 va[(d + 1) & 1] = fp8x8_to_bf16((uint32_t)vw[(d + 1) % 3][0], (uint32_t)vw[(d + 1) % 3][1]);
