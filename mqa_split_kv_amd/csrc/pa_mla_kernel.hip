@@ -226,10 +226,21 @@ __device__ __forceinline__ uint64_t s_mad64(uint64_t a, uint32_t b, uint64_t c)
         : "scc");
     return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ void lds_dma_glb4(const void *g, uint32_t lds)
+// (the row base in scalar registers, the lane's byte offset in a vector register: no 64-bit
+// vector address is kept across the tile loop; the offsets stay below 2^28, since a request
+// has at most 2^26 pages and 2^24 indices)
+__device__ __forceinline__ void lds_dma_glb4(const void *row, uint32_t byte_off, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 ::"s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(row) : "memory", "m0");
+}
+// a row pointer that is the same in every lane, in scalar registers
+template <typename T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p)
+{
+    const uint64_t x = (uint64_t)p;
+    return (const T *)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x));
 }
 
 // 8 e4m3 codes (two words) -> 8 bf16 (exact)
@@ -644,14 +655,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             auto look = [&](int which, int j) {
                 return &s_look[((which * kLookRing + (j & (kLookRing - 1))) * kLoadWaves + lw) * kTokPerWave];
             };
+            const int32_t *bt_row = uniform_ptr(bt + (int64_t)b * a.max_pages);
+            const int32_t *ix_row = SPARSE ? uniform_ptr(indices + (int64_t)b * a.topk) : nullptr;
             auto sp_issue_pos = [&](int j) {           // slots past the row: its last entry
                 if (lane < kTokPerWave)
-                    lds_dma_glb4(indices + (int64_t)b * a.topk + min(sp_slot(j), a.topk - 1), lds_addr(look(0, j)));
+                    lds_dma_glb4(ix_row, 4u * (uint32_t)min(sp_slot(j), a.topk - 1), lds_addr(look(0, j)));
             };
             auto sp_issue_page = [&](int j, int pos) { // no real token: the row's first page
                 const bool ok = sp_slot(j) < t1 && pos >= 0 && pos < Lb;
                 if (lane < kTokPerWave)
-                    lds_dma_glb4(bt + (int64_t)b * a.max_pages + (ok ? pos >> a.page_shift : 0), lds_addr(look(1, j)));
+                    lds_dma_glb4(bt_row, 4u * (uint32_t)(ok ? pos >> a.page_shift : 0), lds_addr(look(1, j)));
             };
             auto sp_read = [&](int which, int j) {     // a lookup that is in; lane l: token l % 4
                 int v;
@@ -661,7 +674,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             };
             auto dn_issue_page = [&](int j) {          // past the item: its last token's page
                 if (lane == 0)
-                    lds_dma_glb4(bt + (int64_t)b * a.max_pages + (min(t0 + kT * j + kTokPerWave * lw, t1 - 1) >> a.page_shift),
+                    lds_dma_glb4(bt_row, 4u * (uint32_t)(min(t0 + kT * j + kTokPerWave * lw, t1 - 1) >> a.page_shift),
                                  lds_addr(look(1, j)));
             };
             // dense: the page id of tile t (uniform), read from LDS; the value exists only after
