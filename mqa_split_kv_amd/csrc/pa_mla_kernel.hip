@@ -424,6 +424,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                 //      converted in the slot before, codes are read 3 slots before that.
                 //      step(k) runs in slot k, before its MFMA: the VALU work of the previous
                 //      tile, issued while the matrix core works.
+                // the token scales of the tile whose S^T was computed last (token 8g4 + 4sb + r,
+                // tiles u = 0..3): written by qk_tile, used by its tile's combine and, one
+                // iteration later, by that tile's P^T scaling
+                f32x4 sc4[4];
                 auto qk_tile = [&](int t_slot, float (&st)[4], auto &&step) {
                     PA_LDS const uint8_t *slot = (PA_LDS const uint8_t *)raw[t_slot];
                     auto rd_codes = [&](int u) {
@@ -439,15 +443,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     u32x4x2 kc[2];                     // codes of tiles u (kc[u & 1])
                     bf16x8 kr[2];
                     f32x4 part[5];
-                    float scu[2][4];                   // scale of tile u of token 8g4 + 4sb + r
+                    float scu0[4];                     // scale of tile 0 of token 8g4 + 4sb + r
                     float x[4];
 #pragma unroll
                     for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    auto rd_scales = [&](int u) {
-#pragma unroll
-                        for (int r = 0; r < 4; r++)
-                            scu[u & 1][r] = *(PA_LDS const float *)(slot + sc_off + r * kRowStep + 4 * u);
-                    };
                     kr[0] = *(PA_LDS const bf16x8 *)(slot + rope_off);
                     kr[1] = *(PA_LDS const bf16x8 *)(slot + rope_off + 64);
                     kc[0] = rd_codes(0);
@@ -456,9 +455,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     for (int k = 0; k < 18; k++) {
                         const int j = k - 2;           // latent step of slot k >= 2
                         // reads issued at this slot: the next tile's codes 3 slots before their
-                        // conversion, the scales of tile u after its MFMAs start
+                        // conversion; the scales of tile 0 after its MFMAs start, the 4 tiles'
+                        // scales of each token (one 16-byte row) once the previous tile's P^T
+                        // scaling (steps 6 - 9) is done with sc4
                         if (j >= 0 && (j & 3) == 0 && j + 4 < 16) kc[((j >> 2) + 1) & 1] = rd_codes((j >> 2) + 1);
-                        if (j >= 0 && (j & 3) == 1) rd_scales(j >> 2);
+                        if (j == 1) {
+#pragma unroll
+                            for (int r = 0; r < 4; r++) scu0[r] = *(PA_LDS const float *)(slot + sc_off + r * kRowStep);
+                        }
+                        if (k == 10) {
+#pragma unroll
+                            for (int r = 0; r < 4; r++) sc4[r] = *(PA_LDS const f32x4 *)(slot + sc_off + r * kRowStep);
+                        }
                         step(k);
                         if (k < 2) {
                             part[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qrope[k], part[4], 0, 0, 0);
@@ -473,7 +481,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
                             for (int r = 0; r < 4; r++) {
                                 float y = u == 0 ? part[4][r] : x[r];
-                                y += scu[u & 1][r] * part[u][r];
+                                y += (u == 0 ? scu0[r] : sc4[r][u]) * part[u][r];
                                 asm volatile("" : "+v"(y));    // computed in this slot
                                 x[r] = y;
                             }
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         __builtin_amdgcn_sched_barrier(0);
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; r++) st[r] = x[r] + scu[1][r] * part[3][r];
+                    for (int r = 0; r < 4; r++) st[r] = x[r] + sc4[r][3] * part[3][r];
                 };
 
                 // ---- logits of row block sb of tile t (log2 domain, masked) and their max per
@@ -534,7 +542,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     //      holds zeros and its result is unused.)
                     float bm_other = 0.f, m_new = m, alpha = 1.f, mref = 0.f, ps = 0.f;
                     float pr[4];
-                    f32x4 scr[2];                      // tile i's token scales, read again
                     bf16x4 pb[4];
                     auto softmax_step = [&](int s) {
                         if (s == 0) bm_other = s_tmax[par][sb ^ 1][hg][col];
@@ -557,14 +564,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         }
                         // the value waves' B operands: P^T times each value tile's token scales
                         // (the value is the key's first 512 dims, so the scales are the key tile
-                        // scales), from the scale rows read again one step before their use (row
-                        // q read in step 5 + q into scr[q & 1], used in step 6 + q)
-                        if (s >= 5 && s < 9)
-                            scr[(s - 5) & 1] = *(PA_LDS const f32x4 *)((PA_LDS const uint8_t *)raw[slot_i] + sc_off + (s - 5) * kRowStep);
+                        // scales, kept in sc4 from tile i's S^T)
                         if (s >= 6 && s < 10) {
                             const int r = s - 6;
 #pragma unroll
-                            for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * scr[r & 1][t]);
+                            for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * sc4[r][t]);
                         }
                         if (s == 11 || s == 12) {
 #pragma unroll
