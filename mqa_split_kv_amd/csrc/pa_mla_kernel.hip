@@ -443,7 +443,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     u32x4x2 kc[2];                     // codes of tiles u (kc[u & 1])
                     bf16x8 kr[2];
                     f32x4 part[5];
-                    float scu0[4];                     // scale of tile 0 of token 8g4 + 4sb + r
                     float x[4];
 #pragma unroll
                     for (int p = 0; p < 5; p++) part[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -455,15 +454,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     for (int k = 0; k < 18; k++) {
                         const int j = k - 2;           // latent step of slot k >= 2
                         // reads issued at this slot: the next tile's codes 3 slots before their
-                        // conversion; the scales of tile 0 after its MFMAs start, the 4 tiles'
-                        // scales of each token (one 16-byte row) once the previous tile's P^T
-                        // scaling (steps 6 - 9) is done with sc4
+                        // conversion; the 4 tiles' scales of each token (one 16-byte row) once
+                        // the previous tile's P^T scaling (steps 4 - 7) is done with sc4
                         if (j >= 0 && (j & 3) == 0 && j + 4 < 16) kc[((j >> 2) + 1) & 1] = rd_codes((j >> 2) + 1);
-                        if (j == 1) {
-#pragma unroll
-                            for (int r = 0; r < 4; r++) scu0[r] = *(PA_LDS const float *)(slot + sc_off + r * kRowStep);
-                        }
-                        if (k == 10) {
+                        if (k == 8) {
 #pragma unroll
                             for (int r = 0; r < 4; r++) sc4[r] = *(PA_LDS const f32x4 *)(slot + sc_off + r * kRowStep);
                         }
@@ -474,14 +468,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                             part[j >> 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j & 1], qb[j >> 2][j & 3], part[j >> 2], 0, 0, 0);
                         }
                         if (k >= 1 && j + 1 < 16) av[(j + 1) & 1] = cvt(kc[((j + 1) >> 2) & 1], (j + 1) & 3);
-                        // the token scales times the tile partials, three slots after a tile's
-                        // last MFMA (tile 3's after the loop); the rope partial starts the sum
-                        if (k == 8 || k == 12 || k == 16) {
-                            const int u = (k - 8) >> 2;
+                        // the token scales times the tile partials: tile 0's five slots after
+                        // its last MFMA (two after its scales are read), tiles 1 and 2 three
+                        // slots after, tile 3's after the loop; the rope partial starts the sum
+                        if (k == 10 || k == 12 || k == 16) {
+                            const int u = k == 10 ? 0 : (k - 8) >> 2;
 #pragma unroll
                             for (int r = 0; r < 4; r++) {
                                 float y = u == 0 ? part[4][r] : x[r];
-                                y += (u == 0 ? scu0[r] : sc4[r][u]) * part[u][r];
+                                y += sc4[r][u] * part[u][r];
                                 asm volatile("" : "+v"(y));    // computed in this slot
                                 x[r] = y;
                             }
@@ -565,8 +560,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         // the value waves' B operands: P^T times each value tile's token scales
                         // (the value is the key's first 512 dims, so the scales are the key tile
                         // scales, kept in sc4 from tile i's S^T)
-                        if (s >= 6 && s < 10) {
-                            const int r = s - 6;
+                        if (s >= 4 && s < 8) {
+                            const int r = s - 4;
 #pragma unroll
                             for (int t = 0; t < 4; t++) pb[t][r] = (__bf16)(pr[r] * sc4[r][t]);
                         }
