@@ -79,6 +79,7 @@
 #include "pa_internal.h"
 #include "pa_merge.h"
 
+#include <cfloat>
 #include <utility>
 
 namespace pa {
@@ -413,7 +414,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                     for (int r = 0; r < 2; r++)
                         qrope[r] = active ? *(const bf16x8 *)(qrow + 512 + 32 * r + 8 * g4) : bf16x8{};
                 }
-                float m = -INFINITY;     // reference max (log2 domain) of head `col`, both halves
+                // reference max (log2 domain) of head `col`, both halves; starts at the lowest
+                // finite value, so that the reference and the factor need no -inf case
+                float m = -FLT_MAX;
                 float l = 0.f;           // this lane's share of the row sum (its 4 tokens)
 
                 // ---- S^T of row block sb of tile t (rows: this lane's tokens 8g4 + 4sb + r) into
@@ -543,15 +546,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
                         if (s == 2) {
                             const float bm = max_nc(bm_own, bm_other);
                             m_new = bm > m + kLazyMax ? bm : m;
-                            alpha = m_new == m ? 1.f : fast_exp2(m - m_new);   // m = -inf: 0
-                            mref = m_new == -INFINITY ? 0.f : m_new;
+                            alpha = fast_exp2(m - m_new);      // exactly 1 if unmoved, 0 from the start
+                            mref = m_new;
                         }
                         if (s == 3 || s == 4) {
 #pragma unroll
-                            for (int r = 2 * (s - 3); r < 2 * (s - 3) + 2; r++) {
-                                pr[r] = fast_exp2(fmaf(sv[r], a.scale_log2, -mref));
-                                ps += pr[r];
-                            }
+                            for (int r = 2 * (s - 3); r < 2 * (s - 3) + 2; r++) pr[r] = fast_exp2(fmaf(sv[r], a.scale_log2, -mref));
+                            ps = s == 3 ? pr[0] + pr[1] : ps + (pr[2] + pr[3]);
                         }
                         if (s == 5) {
                             l = l * alpha + ps;
